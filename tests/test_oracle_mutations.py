@@ -1,0 +1,85 @@
+"""Planted mistakes in the oracle (CPU only): each one must make a pin fail.
+
+This shows the pins are sensitive to the plausible slips named in the oracle's
+readings: a dropped scale, the wrong GQA head mapping, a flipped rescale sign,
+a normalised partial O, an off-by-one compute end, a wrong merge order in the
+fan-out, and the L^2/2 pair count."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.attention as oatt
+import oracle.decode as odec
+import oracle.triplet as otri
+import oracle.worklist as owl
+from oracle import Triplet
+from tests import test_oracle_attention as A
+from tests import test_oracle_triplet as TR
+from tests import test_oracle_worklist_decode as WD
+
+
+def _fails(fn, *args):
+    with pytest.raises(AssertionError):
+        fn(*args)
+
+
+def test_dropped_scale_is_caught(monkeypatch):
+    monkeypatch.setattr(oatt, "softmax_scale", lambda d: 1.0)
+    _fails(A.test_torch_sdpa_float64, False, (1, 1))
+    _fails(A.test_hand_fixtures)
+
+
+def test_wrong_gqa_mapping_is_caught(monkeypatch):
+    monkeypatch.setattr(oatt, "kv_head_of", lambda h, hq, hkv: h % hkv)
+    _fails(A.test_gqa_equals_repeated_mha)
+    _fails(A.test_brute_force_tiny, 4, 4, 2, (4, 2), False)
+
+
+def test_flipped_rescale_sign_is_caught(monkeypatch):
+    def bad_merge(a, b):
+        m = np.maximum(a.m, b.m)
+        shift = np.where(np.isfinite(m), m, 0.0)
+        sa, sb = np.exp(shift - a.m), np.exp(b.m - shift)
+        sa = np.where(np.isfinite(sa), sa, 0.0)
+        return Triplet(m, a.l * sa + b.l * sb, a.O * sa[:, None] + b.O * sb[:, None])
+    monkeypatch.setattr(otri, "merge_ref", bad_merge)
+    _fails(TR.test_ring_equals_monolithic, 4, False, (1, 1))
+
+
+def test_normalised_partial_is_caught(monkeypatch):
+    good = otri.partial_ref
+
+    def normalised(qr, kk, vv, allowed, scale):
+        t = good(qr, kk, vv, allowed, scale)
+        l = np.where(t.l > 0, t.l, 1.0)
+        return Triplet(t.m, t.l, t.O / l[:, None])
+    monkeypatch.setattr(otri, "partial_ref", normalised)
+    _fails(TR.test_ring_equals_monolithic, 4, False, (1, 1))
+
+
+def test_off_by_one_compute_end_is_caught(monkeypatch):
+    good = owl.worklist_ref
+
+    def bad(seq_offsets, BQ):
+        return [owl.WorkItem(i.seq, i.tile, i.range_start, i.range_len, i.tile_start,
+                             i.tile_extent, i.compute_end - 1) for i in good(seq_offsets, BQ)]
+    monkeypatch.setattr(owl, "worklist_ref", bad)
+    _fails(WD.test_worklist_hand_fixture)
+
+
+def test_unordered_worklist_is_caught(monkeypatch):
+    good = owl.worklist_ref
+    monkeypatch.setattr(owl, "worklist_ref", lambda o, BQ: sorted(good(o, BQ), key=lambda i: (i.seq, i.tile)))
+    _fails(WD.test_worklist_hand_fixture)
+
+
+def test_wrong_fanout_order_is_caught(monkeypatch):
+    bad = lambda r, n: [r] + [o for o in range(n) if o != r]
+    monkeypatch.setattr(odec, "fanout_order", bad)
+    monkeypatch.setattr(oracle, "fanout_order", bad)
+    _fails(WD.test_fanout_exactly_once_and_replicated, 4)
+
+
+def test_half_square_pair_count_is_caught(monkeypatch):
+    monkeypatch.setattr(oracle, "causal_pairs", lambda L: L * L // 2)
+    _fails(WD.test_counts_closed_forms_and_brute_force)
