@@ -1,0 +1,68 @@
+// fakv_kernels.h -- kernel parameter blocks and launchers (library-internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <atomic>
+
+namespace fakv {
+
+// Parameters of one prefill launch.  Dense batches (items == nullptr) have
+// n_seqs sequences of T_q queries / S_kv keys; jagged batches read their
+// (sequence, query tile) items from a device worklist.
+struct PrefillParams {
+  const uint16_t* q;       // bf16 bits, or fp32 via the f32 kernels' cast
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;             // mode 0: output in the input dtype
+  float* m_st;             // modes 1, 2: triplet state (T, h_q)
+  float* l_st;             //                            (T, h_q)
+  float* o_st;             //                            (T, h_q, d)
+  int mode;                // 0 = O / l, 1 = write triplet, 2 = merge into triplet
+  int n_seqs, T_q, S_kv;
+  int h_q, h_kv;
+  int C, causal, prune;
+  int q_pos0, k_pos0;
+  const int32_t* items;    // jagged worklist records (8 x int32), or nullptr
+  const int32_t* n_items;  // device count of records
+  int n_qtiles;            // dense: query tiles per sequence
+  int n_hg;                // workgroups per query tile = h_q / heads per workgroup
+  float scale;             // 1 / sqrt(d)
+  float scale_log2;        // scale * log2(e)
+};
+
+struct DecodeParams {
+  const uint16_t* q;       // (B, h_q, d) bf16
+  const uint16_t* k;       // (B, S, h_kv, d)
+  const uint16_t* v;
+  float* m_parts;          // (n_chunks, B*h_q)
+  float* l_parts;
+  float* o_parts;          // (n_chunks, B*h_q, d)
+  int B, h_q, h_kv, S, n_chunks, chunk_w;
+  float scale, scale_log2;
+};
+
+struct MergeParams {
+  const float* m_parts;
+  const float* l_parts;
+  const float* o_parts;
+  int n_parts, rows;
+  void* o_out;
+  float* lse_out;
+  int out_bf16;
+};
+
+// Per-device one-time raise of a kernel's dynamic-LDS limit.
+hipError_t ensure_lds_limit(const void* fn, int bytes, std::atomic<unsigned>& done_mask);
+
+int prefill_bf16_block_k(int d);
+hipError_t launch_prefill_bf16(const PrefillParams& p, int d, int qh, int grid, hipStream_t stream);
+hipError_t launch_prefill_f32(const PrefillParams& p, int d, int grid, hipStream_t stream);
+constexpr int kF32QueryTile = 128;   // query rows per fp32 workgroup
+hipError_t launch_decode_partial(const DecodeParams& p, int d, int g, hipStream_t stream);
+hipError_t launch_lse_merge(const MergeParams& p, int d, hipStream_t stream);
+hipError_t launch_worklist(const int32_t* seq_offsets, int n_seqs, int total, int BQ,
+                           int32_t* items, int32_t* n_items, int capacity, hipStream_t stream);
+
+}  // namespace fakv

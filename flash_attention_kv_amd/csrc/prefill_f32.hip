@@ -1,0 +1,234 @@
+// prefill_f32.hip -- fp32 blockwise prefill attention (fp32 in, fp32 out).
+//
+// Same walk as the bf16 kernel (ring chunk order, dependent causal end, tail
+// masks, jagged items, triplet modes), evaluated in fp32 end to end on the
+// fp32 MFMA (v_mfma_f32_32x32x2f32: products and sums in fp32, no operand
+// rounding).  With a contraction depth of 2 per instruction each lane holds a
+// single k-value per operand, so V needs no transposition: for the value
+// product O^T += V^T P^T the lane's own P register is the B operand and V is
+// read row-major.  One workgroup = 4 waves = 128 query rows of one head.
+#include "fakv_device.h"
+#include "fakv_kernels.h"
+
+namespace fakv {
+
+template <int D>
+__global__ __launch_bounds__(256, 1)
+void prefill_f32_kernel(PrefillParams p) {
+  constexpr int BK = 32;               // keys per tile (one MFMA block)
+  constexpr int BQ = 128;
+  constexpr int DB = D / 32;
+  constexpr int KST = D + 2;           // LDS row stride (floats) of K: conflict-free column reads
+  constexpr int VST = D + 8;           // LDS row stride (floats) of V
+  constexpr int KBYTES = BK * KST * 4;
+  constexpr int VBYTES = BK * VST * 4;
+  constexpr int NCH = D / 4;           // 16-byte chunks per row
+  constexpr int CH = BK * NCH / 256;   // chunks per thread per tensor
+  static_assert(CH * 256 == BK * NCH, "tile/threads mismatch");
+
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const float* Q = reinterpret_cast<const float*>(p.q);
+  const float* K = reinterpret_cast<const float*>(p.k);
+  const float* V = reinterpret_cast<const float*>(p.v);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, col = lane & 31;
+
+  int seq_q0, seq_k0, Lq, Lk, q_lo, q_hi, head;
+  if (p.items != nullptr) {
+    const int item = blockIdx.x / p.n_hg;
+    head = blockIdx.x - item * p.n_hg;
+    if (item >= *p.n_items) return;
+    const int32_t* it = p.items + 8 * (size_t)item;
+    seq_q0 = seq_k0 = it[2];
+    Lq = Lk = it[3];
+    q_lo = it[4] - it[2];
+    q_hi = it[6] - it[2];
+  } else {
+    const int pairs = p.n_seqs * p.n_hg;
+    const int qt_rev = blockIdx.x / pairs;
+    const int pair = blockIdx.x - qt_rev * pairs;
+    const int qt = p.n_qtiles - 1 - qt_rev;
+    const int seq = pair / p.n_hg;
+    head = pair - seq * p.n_hg;
+    seq_q0 = seq * p.T_q; seq_k0 = seq * p.S_kv;
+    Lq = p.T_q; Lk = p.S_kv;
+    q_lo = qt * BQ;
+    q_hi = min(q_lo + BQ, Lq);
+  }
+  const int kvh = head / (p.h_q / p.h_kv);
+  const int delta = p.q_pos0 - p.k_pos0;
+  const int w = (p.items != nullptr) ? (Lk + p.C - 1) / p.C : Lk / p.C;
+
+  KvWalk walk;
+  walk.S = Lk; walk.C = p.C; walk.w = w;
+  walk.r = (Lq > 0) ? (int)(((long long)q_lo * p.C) / Lq) : 0;
+  walk.q_hi = q_hi; walk.delta = delta; walk.causal = p.causal; walk.prune = p.prune;
+  walk.BK = BK;
+  walk.first();
+
+  const int qw_lo = q_lo + 32 * wave;
+  const int qw_hi = min(qw_lo + 32, q_hi);
+  const bool wave_active = qw_lo < q_hi;
+  const int qi = qw_lo + col;
+  const bool qvalid = qi < q_hi;
+  const size_t qrow = (size_t)(seq_q0 + qi) * p.h_q + head;
+
+  // Q^T as B operands: k-step s covers dims 2s, 2s+1; this lane holds dim 2s + half.
+  float qreg[D / 2];
+#pragma unroll
+  for (int s = 0; s < D / 2; ++s) qreg[s] = qvalid ? Q[qrow * D + 2 * s + half] : 0.f;
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int b = 0; b < DB; ++b) oacc[b] = f32x16{};
+  float m_run = neg_inf(), l_run = 0.f;
+  if (p.mode == 2 && qvalid) {
+    m_run = p.m_st[qrow];
+    l_run = half == 0 ? p.l_st[qrow] : 0.f;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        oacc[b][r] = p.o_st[qrow * D + 32 * b + 8 * (r >> 2) + 4 * half + (r & 3)];
+  }
+
+  const size_t kv_stride = (size_t)p.h_kv * D;
+  const float* kbase = K + ((size_t)seq_k0 * p.h_kv + kvh) * D;
+  const float* vbase = V + ((size_t)seq_k0 * p.h_kv + kvh) * D;
+  f32x4 kst[CH], vst[CH];
+  auto load_tile = [&](int kt, int lim) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int id = tid + 256 * i;
+      const int r = id / NCH, c = id % NCH;
+      f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
+      if (kt + r < lim) {
+        a = *reinterpret_cast<const f32x4*>(kbase + (size_t)(kt + r) * kv_stride + 4 * c);
+        b = *reinterpret_cast<const f32x4*>(vbase + (size_t)(kt + r) * kv_stride + 4 * c);
+      }
+      kst[i] = a; vst[i] = b;
+    }
+  };
+  auto store_tile = [&](int buf) {
+    float* kl = reinterpret_cast<float*>(smem + buf * (KBYTES + VBYTES));
+    float* vl = reinterpret_cast<float*>(smem + buf * (KBYTES + VBYTES) + KBYTES);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int id = tid + 256 * i;
+      const int r = id / NCH, c = id % NCH;
+      f32x2 lo = {kst[i][0], kst[i][1]}, hi = {kst[i][2], kst[i][3]};
+      *reinterpret_cast<f32x2*>(kl + r * KST + 4 * c) = lo;
+      *reinterpret_cast<f32x2*>(kl + r * KST + 4 * c + 2) = hi;
+      *reinterpret_cast<f32x4*>(vl + r * VST + 4 * c) = vst[i];
+    }
+  };
+
+  const float scale = p.scale, scale_log2 = p.scale_log2;
+  if (walk.valid) { load_tile(walk.kt, walk.end); store_tile(0); }
+  __syncthreads();
+
+  int buf = 0;
+  while (walk.valid) {
+    const int kt = walk.kt, end = walk.end;
+    KvWalk nxt = walk;
+    nxt.next();
+    if (nxt.valid) load_tile(nxt.kt, nxt.end);
+
+    const bool skip = !wave_active || (p.causal && p.prune && kt > qw_hi - 1 + delta);
+    if (!skip) {
+      const float* kl = reinterpret_cast<const float*>(smem + buf * (KBYTES + VBYTES));
+      const float* vl = reinterpret_cast<const float*>(smem + buf * (KBYTES + VBYTES) + KBYTES);
+      f32x16 sacc = f32x16{};
+#pragma unroll
+      for (int s = 0; s < D / 2; ++s) sacc = mfma32x32x2f32(kl[col * KST + 2 * s + half], qreg[s], sacc);
+      const bool need_mask = (kt + BK > end) || (p.causal && (kt + BK - 1 > qw_lo + delta));
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kt + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (!(key < end && (!p.causal || key <= qi + delta))) sacc[r] = neg_inf();
+        }
+      }
+      float mt = neg_inf();
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[r]);
+      mt = fmaxf(mt, xor32(mt));
+      const float m_new = fmaxf(m_run, mt * scale);
+      const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
+      const float alpha = fast_exp2((m_run - m_use) * kLog2e);
+      const float mlog = m_use * kLog2e;
+      float rs = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = fast_exp2(__builtin_fmaf(sacc[r], scale_log2, -mlog));
+        sacc[r] = e;
+        rs += e;
+      }
+      l_run = l_run * alpha + rs;
+      m_run = m_new;
+#pragma unroll
+      for (int b = 0; b < DB; ++b) {
+        f32x16 acc = oacc[b] * alpha;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 8 * (r >> 2) + 4 * half + (r & 3);
+          acc = mfma32x32x2f32(vl[key * VST + 32 * b + col], sacc[r], acc);
+        }
+        oacc[b] = acc;
+      }
+    }
+    if (nxt.valid) store_tile(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    walk = nxt;
+  }
+
+  const float l_tot = l_run + xor32(l_run);
+  if (!qvalid) return;
+  if (p.mode == 0) {
+    const float inv = 1.f / l_tot;
+    float* op = reinterpret_cast<float*>(p.o) + qrow * D + 4 * half;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 x = {oacc[b][4 * g] * inv, oacc[b][4 * g + 1] * inv, oacc[b][4 * g + 2] * inv,
+                   oacc[b][4 * g + 3] * inv};
+        *reinterpret_cast<f32x4*>(op + 32 * b + 8 * g) = x;
+      }
+  } else {
+    if (half == 0) { p.m_st[qrow] = m_run; p.l_st[qrow] = l_tot; }
+    float* os = p.o_st + qrow * D + 4 * half;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 x = {oacc[b][4 * g], oacc[b][4 * g + 1], oacc[b][4 * g + 2], oacc[b][4 * g + 3]};
+        *reinterpret_cast<f32x4*>(os + 32 * b + 8 * g) = x;
+      }
+  }
+}
+
+template <int D>
+static hipError_t launch_f32(const PrefillParams& p, int grid, hipStream_t stream) {
+  constexpr int smem = 2 * (32 * (D + 2) * 4 + 32 * (D + 8) * 4);
+  static std::atomic<unsigned> lds_done{0};
+  auto kern = prefill_f32_kernel<D>;
+  hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), smem, lds_done);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), smem, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_f32(const PrefillParams& p, int d, int grid, hipStream_t stream) {
+  switch (d) {
+    case 64: return launch_f32<64>(p, grid, stream);
+    case 128: return launch_f32<128>(p, grid, stream);
+    case 256: return launch_f32<256>(p, grid, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fakv
