@@ -1,0 +1,259 @@
+"""Benchmark of the blockwise-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads a,b] [--no-cpu-baseline]
+
+One "step" is one call of the library on one batch of synthetic, device-
+resident input.  The headline line is the GQA ring prefill workload (32 query
+heads over 8 KV heads, d = 128, 8192 tokens split into 8 ring chunks, bf16,
+causal): its value is useful causal TFLOP/s (4 d h_q per admissible
+(query, key) pair).  The same run measures, as extra entries, the dense causal
+d = 256 workload, the jagged 1152-sequence workload, the split-KV decode
+workload (HBM GB/s) and the 4-chunk fp32 ring latency case.
+
+Timing: W untimed warm-up steps, then K steps, each bracketed by HIP events
+recorded on the stream the library launches on (torch's current stream); the
+timed region is bracketed by device synchronisation.  `roofline.achieved` is
+the dominant kernel's algorithmic work per launch over its average event-timed
+duration.  `roofline.traffic` comes from the committed rocprofv3 counter
+summary when it was taken on the current kernel sources, else null.
+`cpu_baseline` times the fp64 NumPy oracle as it stands on a bounded sample of
+the headline workload (whole query heads, all rows), on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+METRIC = "useful causal TFLOP/s (prefill) and HBM GB/s (split-KV decode), % of roofline"
+
+
+def csrc_hash() -> str:
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "flash_attention_kv_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        h.update(f.encode())
+        h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    measured on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        data = json.load(open(p))
+    except ValueError:
+        return None
+    ent = data.get(workload)
+    if not ent or ent.get("csrc_hash") != csrc_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def time_steps(fn, steps: int, warmup: int, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) for a, b in evs]
+    return sum(per) / len(per), wall
+
+
+def bench_prefill(name, steps, warmup, keep=False):
+    import numpy as np
+    import torch
+    import flash_attention_kv_amd as F
+    from workloads import WORKLOADS, make_prefill_inputs
+    w = WORKLOADS[name]
+    q, k, v, offs = make_prefill_inputs(w, device="cuda")
+    o = torch.empty_like(q)
+    offs_t = torch.from_numpy(offs).to("cuda") if offs is not None else None
+    tq, sk = (w.T_q, w.S_kv) if offs is None else (q.shape[0], q.shape[0])
+    dt = F.BF16 if w.dtype == "bf16" else F.F32
+    need = F.ring_attn_workspace_bytes(tq, sk, w.h_q, w.h_kv, w.d, w.C, w.causal, w.n_seqs,
+                                       offs is not None, dt)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        F.ring_attn_fwd(q, k, v, C=w.C, causal=w.causal, seq_offsets=offs_t, n_seqs=w.n_seqs,
+                        workspace=ws, out=o)
+
+    ms, wall = time_steps(step, steps, warmup, stream)
+    if offs is not None:
+        L = np.diff(offs.astype(np.int64))
+        pairs = int((L * (L + 1) // 2).sum()) if w.causal else int((L * L).sum())
+    else:
+        pairs = w.n_seqs * (w.T_q * (w.T_q + 1) // 2 if w.causal else w.T_q * w.S_kv)
+    flops = 4 * w.d * w.h_q * pairs
+    res = dict(ms=ms, wall_s=wall, flops=flops, tflops=flops / (ms * 1e-3) / 1e12, launches=1 if offs is None else 2)
+    if keep:
+        res["tensors"] = (q, k, v)
+    else:
+        del q, k, v, o, ws
+        torch.cuda.empty_cache()
+    return res
+
+
+def bench_decode(steps, warmup):
+    import torch
+    import flash_attention_kv_amd as F
+    from workloads import WORKLOADS, make_decode_inputs
+    w = WORKLOADS["decode"]
+    q, k, v = make_decode_inputs(w, device="cuda")
+    o = torch.empty_like(q)
+    ws = torch.empty(F.splitkv_decode_workspace_bytes(w.B, w.h_q, w.d, w.n_chunks), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        F.splitkv_decode(q, k, v, n_chunks=w.n_chunks, workspace=ws, out=o)
+
+    ms, wall = time_steps(step, steps, warmup, stream)
+    kv_bytes = 2 * w.B * w.S_cache * w.h_kv * w.d * 2
+    alg = kv_bytes + 2 * w.B * w.h_q * w.d * 2
+    parts = 2 * w.n_chunks * w.B * w.h_q * (w.d + 2) * 4      # triplets written, then read
+    del q, k, v, o, ws
+    torch.cuda.empty_cache()
+    return dict(ms=ms, wall_s=wall, bytes=alg, partial_bytes=parts, gbs=alg / (ms * 1e-3) / 1e9)
+
+
+def cpu_baseline(tensors, budget_s: float = 12.0):
+    """Time the fp64 oracle on whole query heads of the headline workload."""
+    import numpy as np
+    import oracle
+    from workloads import WORKLOADS
+    w = WORKLOADS["gqa_ring"]
+    q, k, v = tensors
+    g = w.h_q // w.h_kv
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [(i.get("internal_api"), i.get("num_threads")) for i in threadpool_info()]
+    except Exception:   # pragma: no cover
+        blas = []
+    threads = max([n for _, n in blas if n] or [1])
+    done, t_used, flops = 0, 0.0, 0
+    t_start = time.perf_counter()
+    for h in range(w.h_q):
+        kvh = h // g
+        qh = q[:, h:h + 1].float().cpu().numpy()
+        kh = k[:, kvh:kvh + 1].float().cpu().numpy()
+        vh = v[:, kvh:kvh + 1].float().cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.attention_ref(qh, kh, vh, causal=True)
+        t_used += time.perf_counter() - t0
+        done += 1
+        flops += 4 * w.d * (w.T_q * (w.T_q + 1) // 2)
+        if t_used >= budget_s:
+            break
+    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {w.h_q} query heads of the GQA ring prefill workload (all {w.T_q} "
+                      f"causal query rows each), fp64 NumPy oracle, {t_used:.1f} s; BLAS {blas}; "
+                      f"host cpus {len(os.sched_getaffinity(0))}",
+            "seconds": round(t_used, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workloads", default="gqa_ring,dense_causal,jagged,decode,ring_tiny")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run one device-to-device copy of BYTES (the reference kernel for "
+                         "scaling HBM counters) and exit")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU sharding of the "
+                          "ring and decode paths is not built (see the design notes)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    if not os.path.exists(os.path.join(ROOT, "flash_attention_kv_amd", "libfakv.so")):
+        import __graft_entry__
+        __graft_entry__.build()
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy:
+        x = torch.ones(args.calibrate_copy // 4, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        torch.cuda.synchronize()
+        y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copied_bytes": args.calibrate_copy}))
+        return
+    sel = [s for s in args.workloads.split(",") if s]
+    extra = {}
+    head = None
+    if "gqa_ring" in sel:
+        head = bench_prefill("gqa_ring", args.steps, args.warmup, keep=not args.no_cpu_baseline)
+        print(f"# gqa_ring: {head['ms']:.3f} ms/step, {head['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    for name in ("dense_causal", "jagged"):
+        if name in sel:
+            r = bench_prefill(name, args.steps, args.warmup)
+            print(f"# {name}: {r['ms']:.3f} ms/step, {r['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+            extra[name] = {"value": round(r["tflops"], 2), "unit": "TFLOP/s", "ms_per_step": round(r["ms"], 4),
+                           "useful_flops": r["flops"],
+                           "roofline": {"bound": "mfma", "achieved": round(r["tflops"], 2), "peak": PEAK_BF16_TFLOPS,
+                                        "unit": "TFLOP/s", "frac": round(r["tflops"] / PEAK_BF16_TFLOPS, 4),
+                                        "traffic": load_traffic(name)}}
+    if "dense_causal" in extra:
+        extra["dense_causal"]["page_context"] = "Pallas dense causal flash on the Helion page, same shape, unnamed chip: 225.8 TF/s"
+    if "jagged" in extra:
+        extra["jagged"]["page_context"] = "Helion page jagged table (softmax 'flash' row, unnamed chip, unknown lengths): 97.7 TF/s"
+    if "decode" in sel:
+        r = bench_decode(args.steps, args.warmup)
+        print(f"# decode: {r['ms']:.3f} ms/step, {r['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+        extra["decode"] = {"value": round(r["gbs"], 1), "unit": "GB/s", "ms_per_step": round(r["ms"], 4),
+                           "algorithmic_bytes": r["bytes"], "partial_triplet_bytes": r["partial_bytes"],
+                           "roofline": {"bound": "hbm", "achieved": round(r["gbs"], 1), "peak": PEAK_HBM_GBS,
+                                        "unit": "GB/s", "frac": round(r["gbs"] / PEAK_HBM_GBS, 4),
+                                        "traffic": load_traffic("decode")}}
+    if "ring_tiny" in sel:
+        r = bench_prefill("ring_tiny", args.steps, args.warmup)
+        extra["ring_tiny"] = {"value": round(r["ms"] * 1e3, 2), "unit": "us per call", "dtype": "f32",
+                              "useful_flops": r["flops"]}
+    if head is None:
+        print(json.dumps({"metric": METRIC, "extra": extra}))
+        return
+    cpu = None if args.no_cpu_baseline else cpu_baseline(head.pop("tensors"))
+    line = {
+        "metric": METRIC, "value": round(head["tflops"], 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["ms"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic N(0,1), seeded, generated on the device",
+        "config": {"workload": "gqa_ring_prefill", "h_q": 32, "h_kv": 8, "d_head": 128, "T_q": 8192,
+                   "S_kv": 8192, "ring_chunks": 8, "causal": True, "global_batch": 1, "seq_len": 8192,
+                   "parallelism": "1 GPU (ring ranks laid out on one device)"},
+        "roofline": {"bound": "mfma", "achieved": round(head["tflops"], 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(head["tflops"] / PEAK_BF16_TFLOPS, 4),
+                     "traffic": load_traffic("gqa_ring"),
+                     "kernel": "prefill_bf16_kernel<128,64,4>", "useful_flops_per_launch": head["flops"]},
+        "cpu_baseline": cpu,
+        "extra": extra,
+        "kernel_sources": csrc_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
