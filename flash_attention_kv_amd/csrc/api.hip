@@ -73,6 +73,14 @@ fakv_status check_prefill_common(const void* q, const void* k, const void* v, in
   return FAKV_OK;
 }
 
+// The bf16 prefill kernel addresses one (sequence, KV head)'s keys through a
+// buffer resource with 32-bit byte offsets.
+fakv_status check_kv_extent(long long keys, int h_kv, int d, int dtype) {
+  if (dtype == FAKV_BF16 && keys * h_kv * d * 2 >= (1ll << 31))
+    return fail(FAKV_EUNSUPPORTED, "one sequence's K/V span (%lld keys x %d heads x %d) exceeds 2 GiB", keys, h_kv, d);
+  return FAKV_OK;
+}
+
 fakv::PrefillParams base_params(const void* q, const void* k, const void* v, int h_q, int h_kv,
                                 int d) {
   fakv::PrefillParams p{};
@@ -153,6 +161,7 @@ fakv_status attn_partial(const void* q, const void* k, const void* v, float* m, 
   if (T_q < 0 || S_chunk < 0) return fail(FAKV_EINVAL, "T_q and S_chunk must be >= 0");
   if ((long long)T_q * h_q * d >= (1ll << 40) || (long long)S_chunk * h_kv * d >= (1ll << 40))
     return fail(FAKV_EINVAL, "tensor too large");
+  if ((s = check_kv_extent(S_chunk, h_kv, d, dtype)) != FAKV_OK) return s;
   if (T_q == 0 || (S_chunk == 0 && accumulate)) return FAKV_OK;
   fakv::PrefillParams p = base_params(q, k, v, h_q, h_kv, d);
   p.m_st = m; p.l_st = l; p.o_st = o_acc;
@@ -210,6 +219,7 @@ fakv_status ring_attn_fwd(const void* q, const void* k, const void* v, void* o, 
       return fail(FAKV_EINVAL, "tensor too large");
     if ((long long)n_seqs * T_q >= (1ll << 31) || (long long)n_seqs * S_kv >= (1ll << 31))
       return fail(FAKV_EINVAL, "token count exceeds int32");
+    if ((s = check_kv_extent(S_kv, h_kv, d, dtype)) != FAKV_OK) return s;
     if (T_q == 0) return FAKV_OK;
     fakv::PrefillParams p = base_params(q, k, v, h_q, h_kv, d);
     p.o = static_cast<uint16_t*>(o);
@@ -228,6 +238,7 @@ fakv_status ring_attn_fwd(const void* q, const void* k, const void* v, void* o, 
   if (reinterpret_cast<uintptr_t>(seq_offsets) & 3u)
     return fail(FAKV_EINVAL, "seq_offsets must be 4-byte aligned");
   if ((long long)T_q * h_q * d >= (1ll << 40)) return fail(FAKV_EINVAL, "tensor too large");
+  if ((s = check_kv_extent(S_kv, h_kv, d, dtype)) != FAKV_OK) return s;
   const size_t need = ring_attn_workspace_bytes(T_q, S_kv, h_q, h_kv, d, C, causal, n_seqs, 1, dtype);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(FAKV_EINVAL, "workspace too small: need %zu bytes, got %zu", need, workspace_bytes);

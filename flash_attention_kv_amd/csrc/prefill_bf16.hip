@@ -8,14 +8,18 @@
 // min(chunk end, query tile end) ("[pallas] Support dependent Tile.end bounds
 // in Pallas", "Unroll lowering": the trip count shrinks instead of masking
 // whole tiles).  Per tile:
-//   1. K and V tiles are staged HBM -> registers -> LDS (K swizzled, V
-//      quad-transposed), double-buffered: tile t+1's loads are in flight
-//      while tile t computes.
+//   1. K and V tiles go HBM -> LDS directly (buffer_load_dwordx4 ... lds: no
+//      register staging), double-buffered: tile t+1 is in flight while tile t
+//      computes.  Keys past the tile's valid end are masked.
 //   2. S^T = K Q^T on MFMA (Q resident in registers as the B operand).
 //   3. The online-softmax fold of the prefill page's ring step, with the
 //      block partial folded directly into the running (m, l, O): row max,
-//      exp2 of pre-scaled scores, per-lane partial row sums, rescale of O.
-//   4. O^T += V^T P^T on MFMA (P rounded to bf16 in registers).
+//      exp2 of pre-scaled scores, per-lane partial row sums; O is rescaled
+//      only when some row max of the wave moved.
+//   4. O^T += V^T P^T on MFMA: P^T straight from registers (rounded to bf16),
+//      V^T read from the row-major V tile with the LDS transpose read
+//      ds_read_b64_tr_b16 (a 16-lane group turns 4 keys x 16 dims into
+//      16 dims x 4 keys).
 // Only tiles that straddle the diagonal or the chunk's tail evaluate the
 // element mask.  The epilogue writes O / l in bf16, or the fp32 triplet.
 #include "fakv_device.h"
@@ -23,26 +27,65 @@
 
 namespace fakv {
 
-template <int D, int BK, int QH>
-__global__ __launch_bounds__(256, (D <= 128) ? 2 : 1)
+// Keys per tile by head dim: every K or V tile is 1024 16-byte slots (16 KB).
+template <int D> struct TileK { static constexpr int BK = 8192 / D; };
+
+// Chunk swizzles.  K: chunk c of row r at c ^ (r & 15) (c ^ (r & 7) for
+// d = 64): the 16 lanes of each ds_read_b128 pass read 16 consecutive keys at
+// one chunk and hit 16 distinct 16-byte bank groups.  V: rows r .. r+3 read by
+// one half-wave in a transpose read land in distinct 64-byte bank groups.
+template <int D>
+__device__ __forceinline__ int vmask(int r) {
+  if constexpr (D == 64) return ((r >> 1) & 1) << 2;
+  else return (r & 3) << 2;
+}
+template <int D>
+__device__ __forceinline__ int kmask(int r) {
+  if constexpr (D == 64) return r & 7;
+  else return r & 15;
+}
+
+// One 16-byte load per lane from a buffer resource straight into LDS; lane l
+// writes lds_wave_base + 16 l.  Offsets at or past the resource's size read 0.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, unsigned voff, char* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_wave_base, 16,
+                                           voff, 0, 0, 0);
+}
+
+// Raw buffer over `bytes` bytes at `base` (gfx9 dword3: 32-bit untyped data).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ void wait_dma_and_sync() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
+__device__ __forceinline__ bf16x4 tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 __attribute__((address_space(3)))*)(p));
+}
+
+template <int D, int QH>
+__global__ __launch_bounds__(256, 2)
 void prefill_bf16_kernel(PrefillParams p) {
+  constexpr int BK = TileK<D>::BK;
   constexpr int WPH = 4 / QH;          // waves per query head
   constexpr int BQ = 32 * WPH;         // query rows per tile
   constexpr int KB = BK / 32;          // 32-key MFMA blocks per tile
   constexpr int DS = D / 16;           // k-steps of S^T = K Q^T
   constexpr int DB = D / 32;           // 32-dim blocks of O^T
   constexpr int KS = BK / 16;          // k-steps of O^T += V^T P^T
-  constexpr int TILE_BYTES = BK * D * 2;
+  constexpr int TILE = BK * D * 2;     // bytes of one K or V tile (16 KB)
   constexpr int NCH = D / 8;           // 16-byte chunks per key row
-  constexpr int KCH = BK * NCH / 256;  // K chunks staged per thread
-  constexpr int VT = (BK / 4) * NCH / 256;  // V quad tasks per thread
-  static_assert(KCH * 256 == BK * NCH && VT * 256 == (BK / 4) * NCH, "tile/threads mismatch");
+  constexpr int NI = TILE / 16 / 256;  // DMA instructions per thread per tensor
+  static_assert(TILE == 16384 && NI == 4, "tile geometry");
 
   extern __shared__ __attribute__((aligned(16))) char smem[];  // K0 V0 K1 V1
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = wave / WPH;
   const int qsub = wave % WPH;
   const int half = lane >> 5;
@@ -60,10 +103,27 @@ void prefill_bf16_kernel(PrefillParams p) {
     q_lo = it[4] - it[2];
     q_hi = it[6] - it[2];
   } else {
+    // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs
+    // (workgroup L runs on XCD L % 8).  Group g of (sequence, head-group)
+    // pairs p = 8g .. 8g+7 places pair 8g + x on XCD x, so all query tiles of
+    // one pair -- which read the same K/V -- run on one XCD and share its L2;
+    // within a pair the longest causal tiles go first.
     const int pairs = p.n_seqs * p.n_hg;
-    const int qt_rev = blockIdx.x / pairs;
-    const int pair = blockIdx.x - qt_rev * pairs;
-    const int qt = p.n_qtiles - 1 - qt_rev;      // longest (causal) tiles first
+    const int main_pairs = pairs & ~7;
+    const int L = blockIdx.x;
+    int pair, qr;
+    if (L < main_pairs * p.n_qtiles) {
+      const int slot = L >> 3;
+      const int pl = slot / p.n_qtiles;
+      qr = slot - pl * p.n_qtiles;
+      pair = pl * 8 + (L & 7);
+    } else {
+      const int R = L - main_pairs * p.n_qtiles;
+      const int rp = pairs - main_pairs;
+      qr = R / rp;
+      pair = main_pairs + (R - qr * rp);
+    }
+    const int qt = p.n_qtiles - 1 - qr;
     const int seq = pair / p.n_hg;
     hg = pair - seq * p.n_hg;
     seq_q0 = seq * p.T_q;
@@ -123,64 +183,48 @@ void prefill_bf16_kernel(PrefillParams p) {
       }
   }
 
-  // ---- staging of K/V tiles ------------------------------------------------
-  const size_t kv_stride = (size_t)p.h_kv * D;           // elements between keys
-  const uint16_t* kbase = p.k + ((size_t)seq_k0 * p.h_kv + kvh) * D;
-  const uint16_t* vbase = p.v + ((size_t)seq_k0 * p.h_kv + kvh) * D;
+  // ---- direct HBM -> LDS tile loads ---------------------------------------
+  // Buffer resources span this (sequence, KV head)'s rows only, so rows past
+  // the sequence end read as zero (and are masked); no address can leave the
+  // tensors.  The host guarantees the byte extent fits 31 bits.
+  const unsigned stride_b = (unsigned)p.h_kv * D * 2;    // bytes between keys
+  const size_t head_off = ((size_t)seq_k0 * p.h_kv + kvh) * D;
+  const unsigned extent = Lk > 0 ? (unsigned)(Lk - 1) * stride_b + D * 2 : 0u;
+  const __amdgpu_buffer_rsrc_t rs_k = make_rsrc(p.k + head_off, extent);
+  const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(p.v + head_off, extent);
+  // slot s = (4 i + wave) * 64 + lane of a tile holds row s / NCH, physical chunk s % NCH
+  unsigned voff_k[NI], voff_v[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int sl = (4 * i + wave) * 64 + lane;
+    const int r = sl / NCH, pc = sl % NCH;
+    voff_k[i] = (unsigned)r * stride_b + (unsigned)((pc ^ kmask<D>(r)) * 16);
+    voff_v[i] = (unsigned)r * stride_b + (unsigned)((pc ^ vmask<D>(r)) * 16);
+  }
+  auto issue_tile = [&](int kt, int buf) {
+    char* kl = smem + buf * 2 * TILE;
+    char* vl = kl + TILE;
+    const unsigned t0 = (unsigned)kt * stride_b;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int blk = 4 * i + wave;
+      dma16(rs_k, t0 + voff_k[i], kl + blk * 1024);
+      dma16(rs_v, t0 + voff_v[i], vl + blk * 1024);
+    }
+  };
 
-  u32x4 kst[KCH];
-  u32x4 vst[VT][4];
-  auto load_tile = [&](int kt, int lim) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int id = tid + 256 * i;
-      const int r = id / NCH, c = id % NCH;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (kt + r < lim) x = *reinterpret_cast<const u32x4*>(kbase + (size_t)(kt + r) * kv_stride + 8 * c);
-      kst[i] = x;
-    }
-#pragma unroll
-    for (int i = 0; i < VT; ++i) {
-      const int id = tid + 256 * i;
-      const int kq = id / NCH, c = id % NCH;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 4 * kq + j;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (kt + r < lim) x = *reinterpret_cast<const u32x4*>(vbase + (size_t)(kt + r) * kv_stride + 8 * c);
-        vst[i][j] = x;
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    char* kl = smem + buf * 2 * TILE_BYTES;
-    char* vl = kl + TILE_BYTES;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int id = tid + 256 * i;
-      const int r = id / NCH, c = id % NCH;
-      *reinterpret_cast<u32x4*>(kl + r * (D * 2) + kswz<D>(r, c) * 16) = kst[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VT; ++i) {
-      const int id = tid + 256 * i;
-      const int kq = id / NCH, c = id % NCH;
-      u32x4 t[4];
-      quad_transpose(vst[i], t);
-      char* dst = vl + (kq * D + 8 * c) * 8;
-#pragma unroll
-      for (int pc = 0; pc < 4; ++pc) *reinterpret_cast<u32x4*>(dst + 16 * pc) = t[pc];
-    }
-  };
+  // lane-constant parts of the LDS read addresses
+  const int kread_mask = kmask<D>(col);                 // rows 32b + col
+  const int vg16 = (lane >> 4) & 1, vp = lane & 15;
+  const int vrow = 4 * half + (vp >> 2);                // + 16 ks (+ 8)
+  const int vmsk = vmask<D>(vrow);
+  const int vbyte = (vp & 1) * 8;
 
   const float scale = p.scale;
   const float scale_log2 = p.scale_log2;
 
-  if (walk.valid) {
-    load_tile(walk.kt, walk.end);
-    store_tile(0);
-  }
-  __syncthreads();
+  if (walk.valid) issue_tile(walk.kt, 0);
+  wait_dma_and_sync();
 
   int buf = 0;
   while (walk.valid) {
@@ -188,12 +232,12 @@ void prefill_bf16_kernel(PrefillParams p) {
     const int end = walk.end;
     KvWalk nxt = walk;
     nxt.next();
-    if (nxt.valid) load_tile(nxt.kt, nxt.end);
+    if (nxt.valid) issue_tile(nxt.kt, buf ^ 1);
 
     const bool skip = !wave_active || (p.causal && p.prune && kt > qw_hi - 1 + delta);
     if (!skip) {
-      const char* kl = smem + buf * 2 * TILE_BYTES;
-      const char* vl = kl + TILE_BYTES;
+      const char* kl = smem + buf * 2 * TILE;
+      const char* vl = kl + TILE;
       // S^T = K Q^T
       f32x16 sacc[KB];
 #pragma unroll
@@ -203,7 +247,7 @@ void prefill_bf16_kernel(PrefillParams p) {
 #pragma unroll
         for (int b = 0; b < KB; ++b) {
           const int r = 32 * b + col;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl + r * (D * 2) + kswz<D>(r, 2 * s + half) * 16);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl + r * (D * 2) + ((2 * s + half) ^ kread_mask) * 16);
           sacc[b] = mfma32x32x16(a, qreg[s], sacc[b]);
         }
       }
@@ -229,7 +273,6 @@ void prefill_bf16_kernel(PrefillParams p) {
       mt = fmaxf(mt, xor32(mt));
       const float m_new = fmaxf(m_run, mt * scale);
       const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
-      const float alpha = fast_exp2((m_run - m_use) * kLog2e);
       const float mlog = m_use * kLog2e;
       float rs = 0.f;
 #pragma unroll
@@ -240,12 +283,17 @@ void prefill_bf16_kernel(PrefillParams p) {
           sacc[b][r] = e;
           rs += e;
         }
-      l_run = l_run * alpha + rs;
+      if (__builtin_amdgcn_ballot_w64(m_new != m_run) != 0) {
+        // some row max moved: rescale by exp(m_old - m_new) (0 for an empty state)
+        const float alpha = fast_exp2((m_run - m_use) * kLog2e);
+        l_run *= alpha;
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+      }
+      l_run += rs;
       m_run = m_new;
-#pragma unroll
-      for (int b = 0; b < DB; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
       // O^T += V^T P^T
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -253,21 +301,20 @@ void prefill_bf16_kernel(PrefillParams p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) pv[j] = sacc[ks >> 1][8 * (ks & 1) + j];
         const bf16x8 pb = pack_bf16x8(pv);
-        const char* q0 = vl + ((4 * ks + half) * D) * 8;
-        const char* q1 = vl + ((4 * ks + 2 + half) * D) * 8;
+        const char* r1 = vl + (16 * ks + vrow) * (D * 2) + vbyte;
+        const char* r2 = r1 + 8 * (D * 2);
 #pragma unroll
         for (int b = 0; b < DB; ++b) {
-          const int e = 32 * b + col;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(q0 + e * 8);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(q1 + e * 8);
-          const u32x4 a4 = {lo[0], lo[1], hi[0], hi[1]};
-          oacc[b] = mfma32x32x16(__builtin_bit_cast(bf16x8, a4), pb, oacc[b]);
+          const int coff = ((4 * b + 2 * vg16 + ((vp & 3) >> 1)) ^ vmsk) * 16;
+          const bf16x4 lo = tr16(r1 + coff);
+          const bf16x4 hi = tr16(r2 + coff);
+          const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          oacc[b] = mfma32x32x16(a, pb, oacc[b]);
         }
       }
     }
 
-    if (nxt.valid) store_tile(buf ^ 1);
-    __syncthreads();
+    wait_dma_and_sync();
     buf ^= 1;
     walk = nxt;
   }
@@ -302,10 +349,10 @@ void prefill_bf16_kernel(PrefillParams p) {
   }
 }
 
-template <int D, int BK, int QH>
+template <int D, int QH>
 static hipError_t launch_one(const PrefillParams& p, int grid, hipStream_t stream) {
-  constexpr int smem = 4 * BK * D * 2;
-  auto kern = prefill_bf16_kernel<D, BK, QH>;
+  constexpr int smem = 4 * 16384;
+  auto kern = prefill_bf16_kernel<D, QH>;
   static std::atomic<unsigned> lds_done{0};
   hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), smem, lds_done);
   if (e != hipSuccess) return e;
@@ -313,23 +360,23 @@ static hipError_t launch_one(const PrefillParams& p, int grid, hipStream_t strea
   return hipGetLastError();
 }
 
-template <int D, int BK>
+template <int D>
 static hipError_t launch_qh(const PrefillParams& p, int qh, int grid, hipStream_t stream) {
   switch (qh) {
-    case 1: return launch_one<D, BK, 1>(p, grid, stream);
-    case 2: return launch_one<D, BK, 2>(p, grid, stream);
-    case 4: return launch_one<D, BK, 4>(p, grid, stream);
+    case 1: return launch_one<D, 1>(p, grid, stream);
+    case 2: return launch_one<D, 2>(p, grid, stream);
+    case 4: return launch_one<D, 4>(p, grid, stream);
   }
   return hipErrorInvalidValue;
 }
 
-int prefill_bf16_block_k(int d) { return d == 64 ? 128 : 64; }
+int prefill_bf16_block_k(int d) { return 8192 / d; }
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, int d, int qh, int grid, hipStream_t stream) {
   switch (d) {
-    case 64: return launch_qh<64, 128>(p, qh, grid, stream);
-    case 128: return launch_qh<128, 64>(p, qh, grid, stream);
-    case 256: return launch_qh<256, 64>(p, qh, grid, stream);
+    case 64: return launch_qh<64>(p, qh, grid, stream);
+    case 128: return launch_qh<128>(p, qh, grid, stream);
+    case 256: return launch_qh<256>(p, qh, grid, stream);
   }
   return hipErrorInvalidValue;
 }
