@@ -149,8 +149,9 @@ size_t ring_attn_workspace_bytes(int T_q, int S_kv, int h_q, int h_kv, int d, in
  * o (B, h_q, d) in dtype.  This is the decode page's local partial per rank
  * followed by its (m, l, o) merge, with the ranks laid side by side on one GPU.
  * workspace: at least splitkv_decode_workspace_bytes(B, h_q, d, n_chunks).
- * Preconditions: B >= 1, S_kv >= 1, 1 <= n_chunks <= S_kv, h_q/h_kv <= 32... see
- * fakv_last_error for the exact reason of a rejection.
+ * Preconditions: dtype == FAKV_BF16, B >= 1, S_kv >= 1, 1 <= n_chunks <= S_kv,
+ * h_q / h_kv <= 32 (the query heads of a group are the 32 columns of one
+ * MFMA tile); otherwise FAKV_EINVAL / FAKV_EUNSUPPORTED and nothing enqueued.
  */
 fakv_status splitkv_decode(const void* q, const void* k, const void* v, void* o,
                            int B, int h_q, int h_kv, int d, int S_kv, int n_chunks,
