@@ -14,18 +14,25 @@
 //   2. S^T = K Q^T on MFMA (Q resident in registers as the B operand).
 //   3. The online-softmax fold of the prefill page's ring step, with the
 //      block partial folded directly into the running (m, l, O): row max,
-//      exp2 of pre-scaled scores, per-lane partial row sums; O is rescaled
-//      only when some row max of the wave moved.
+//      exp2 of pre-scaled scores, per-lane partial row sums.  l and O are
+//      kept relative to a lazily moved shift (see kLazyShift), so O is
+//      rescaled only when some row max of the wave outgrows it.
 //   4. O^T += V^T P^T on MFMA: P^T straight from registers (rounded to bf16),
 //      V^T read from the row-major V tile with the LDS transpose read
 //      ds_read_b64_tr_b16 (a 16-lane group turns 4 keys x 16 dims into
 //      16 dims x 4 keys).
 // Only tiles that straddle the diagonal or the chunk's tail evaluate the
 // element mask.  The epilogue writes O / l in bf16, or the fp32 triplet.
+#include <type_traits>
+
 #include "fakv_device.h"
 #include "fakv_kernels.h"
 
 namespace fakv {
+
+// Lazy softmax shift: the running shift moves only when the row max exceeds
+// it by more than this many powers of two.
+constexpr float kLazyShift = 8.f;
 
 // Keys per tile by head dim: every K or V tile is 1024 16-byte slots (16 KB).
 template <int D> struct TileK { static constexpr int BK = 8192 / D; };
@@ -81,7 +88,7 @@ void prefill_bf16_kernel(PrefillParams p) {
   constexpr int NI = TILE / 16 / 256;  // DMA instructions per thread per tensor
   static_assert(TILE == 16384 && NI == 4, "tile geometry");
 
-  extern __shared__ __attribute__((aligned(16))) char smem[];  // K0 V0 K1 V1
+  __shared__ __attribute__((aligned(16))) char smem[4 * TILE];  // K0 V0 K1 V1
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -167,10 +174,16 @@ void prefill_bf16_kernel(PrefillParams p) {
   f32x16 oacc[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b) oacc[b] = f32x16{};
-  float m_run = neg_inf();   // natural-log units of the scaled score
+  // Running state.  m_true is the row max of the scaled scores seen so far;
+  // l and O are kept relative to a shift m_sh <= m_true (all in natural-log
+  // units of the scaled score).  The shift only moves when the max outgrows
+  // it by more than kLazyShift (in log2 units), so exp terms stay <= 2^8 and
+  // most tiles skip the O rescale; O / l does not depend on the shift.
+  float m_true = neg_inf();
+  float m_sh = neg_inf();
   float l_run = 0.f;         // this lane's partial row sum (keys of its half)
   if (p.mode == 2 && qvalid) {
-    m_run = p.m_st[qrow];
+    m_true = m_sh = p.m_st[qrow];
     l_run = half == 0 ? p.l_st[qrow] : 0.f;
     const float* os = p.o_st + qrow * D + 4 * half;
 #pragma unroll
@@ -213,30 +226,39 @@ void prefill_bf16_kernel(PrefillParams p) {
     }
   };
 
-  // lane-constant parts of the LDS read addresses
-  const int kread_mask = kmask<D>(col);                 // rows 32b + col
-  const int vg16 = (lane >> 4) & 1, vp = lane & 15;
-  const int vrow = 4 * half + (vp >> 2);                // + 16 ks (+ 8)
-  const int vmsk = vmask<D>(vrow);
-  const int vbyte = (vp & 1) * 8;
+  // Lane-constant LDS read offsets (bytes within a tile).  The swizzles make
+  // them non-linear in the k-step / dim block, so they are computed once here;
+  // inside the loop every address is one of these plus an immediate.
+  int koff[DS];                                          // + 32 b rows
+#pragma unroll
+  for (int s = 0; s < DS; ++s) koff[s] = col * (D * 2) + (((2 * s + half) ^ kmask<D>(col)) * 16);
+  int voff[DB];                                          // + 16 ks rows (+ 8 rows)
+  {
+    const int vg16 = (lane >> 4) & 1, vp = lane & 15;
+    const int vrow = 4 * half + (vp >> 2);
+    const int vmsk = vmask<D>(vrow);
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+      voff[b] = vrow * (D * 2) + ((4 * b + 2 * vg16 + ((vp & 3) >> 1)) ^ vmsk) * 16 + (vp & 1) * 8;
+  }
 
   const float scale = p.scale;
   const float scale_log2 = p.scale_log2;
 
-  if (walk.valid) issue_tile(walk.kt, 0);
-  wait_dma_and_sync();
-
-  int buf = 0;
-  while (walk.valid) {
+  // One tile of the walk on LDS buffer BUF (a compile-time constant, so LDS
+  // addresses fold into immediates): prefetch the next tile into the other
+  // buffer, compute this one, then wait for the prefetch and synchronise.
+  auto step = [&](auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
     const int kt = walk.kt;
     const int end = walk.end;
     KvWalk nxt = walk;
     nxt.next();
-    if (nxt.valid) issue_tile(nxt.kt, buf ^ 1);
+    if (nxt.valid) issue_tile(nxt.kt, BUF ^ 1);
 
     const bool skip = !wave_active || (p.causal && p.prune && kt > qw_hi - 1 + delta);
     if (!skip) {
-      const char* kl = smem + buf * 2 * TILE;
+      const char* kl = smem + BUF * 2 * TILE;
       const char* vl = kl + TILE;
       // S^T = K Q^T
       f32x16 sacc[KB];
@@ -246,8 +268,7 @@ void prefill_bf16_kernel(PrefillParams p) {
       for (int s = 0; s < DS; ++s) {
 #pragma unroll
         for (int b = 0; b < KB; ++b) {
-          const int r = 32 * b + col;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl + r * (D * 2) + ((2 * s + half) ^ kread_mask) * 16);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl + koff[s] + b * 32 * (D * 2));
           sacc[b] = mfma32x32x16(a, qreg[s], sacc[b]);
         }
       }
@@ -271,29 +292,28 @@ void prefill_bf16_kernel(PrefillParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[b][r]);
       mt = fmaxf(mt, xor32(mt));
-      const float m_new = fmaxf(m_run, mt * scale);
-      const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
-      const float mlog = m_use * kLog2e;
-      float rs = 0.f;
-#pragma unroll
-      for (int b = 0; b < KB; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(__builtin_fmaf(sacc[b][r], scale_log2, -mlog));
-          sacc[b][r] = e;
-          rs += e;
-        }
-      if (__builtin_amdgcn_ballot_w64(m_new != m_run) != 0) {
-        // some row max moved: rescale by exp(m_old - m_new) (0 for an empty state)
-        const float alpha = fast_exp2((m_run - m_use) * kLog2e);
+      m_true = fmaxf(m_true, mt * scale);
+      if (__builtin_amdgcn_ballot_w64(m_true > m_sh + kLazyShift * kLn2) != 0) {
+        // move the shift to the true max: rescale by exp(m_sh - m_true)
+        // (0 for an empty state)
+        const float mu = (m_true == neg_inf()) ? 0.f : m_true;
+        const float alpha = fast_exp2((m_sh - mu) * kLog2e);
+        m_sh = m_true;
         l_run *= alpha;
 #pragma unroll
         for (int b = 0; b < DB; ++b)
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
       }
-      l_run += rs;
-      m_run = m_new;
+      const float mlog = ((m_sh == neg_inf()) ? 0.f : m_sh) * kLog2e;
+#pragma unroll
+      for (int b = 0; b < KB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = fast_exp2(__builtin_fmaf(sacc[b][r], scale_log2, -mlog));
+          sacc[b][r] = e;
+          l_run += e;
+        }
       // O^T += V^T P^T
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -301,26 +321,30 @@ void prefill_bf16_kernel(PrefillParams p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) pv[j] = sacc[ks >> 1][8 * (ks & 1) + j];
         const bf16x8 pb = pack_bf16x8(pv);
-        const char* r1 = vl + (16 * ks + vrow) * (D * 2) + vbyte;
-        const char* r2 = r1 + 8 * (D * 2);
 #pragma unroll
         for (int b = 0; b < DB; ++b) {
-          const int coff = ((4 * b + 2 * vg16 + ((vp & 3) >> 1)) ^ vmsk) * 16;
-          const bf16x4 lo = tr16(r1 + coff);
-          const bf16x4 hi = tr16(r2 + coff);
+          const char* a1 = vl + voff[b] + 16 * ks * (D * 2);
+          const bf16x4 lo = tr16(a1);
+          const bf16x4 hi = tr16(a1 + 8 * (D * 2));
           const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
           oacc[b] = mfma32x32x16(a, pb, oacc[b]);
         }
       }
     }
-
     wait_dma_and_sync();
-    buf ^= 1;
     walk = nxt;
+  };
+
+  if (walk.valid) issue_tile(walk.kt, 0);
+  wait_dma_and_sync();
+  while (walk.valid) {
+    step(std::integral_constant<int, 0>{});
+    if (!walk.valid) break;
+    step(std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue -------------------------------------------------------------
-  const float l_tot = l_run + xor32(l_run);
+  float l_tot = l_run + xor32(l_run);
   if (!qvalid) return;
   if (p.mode == 0) {
     const float inv = 1.f / l_tot;
@@ -334,8 +358,11 @@ void prefill_bf16_kernel(PrefillParams p) {
         *reinterpret_cast<u32x2*>(op + 32 * b + 8 * g) = x;
       }
   } else {
+    // exported triplets are relative to the true row max
+    const float f = (m_true == neg_inf()) ? 1.f : fast_exp2((m_sh - m_true) * kLog2e);
+    l_tot *= f;
     if (half == 0) {
-      p.m_st[qrow] = m_run;
+      p.m_st[qrow] = m_true;
       p.l_st[qrow] = l_tot;
     }
     float* os = p.o_st + qrow * D + 4 * half;
@@ -343,7 +370,7 @@ void prefill_bf16_kernel(PrefillParams p) {
     for (int b = 0; b < DB; ++b)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        f32x4 x = {oacc[b][4 * g], oacc[b][4 * g + 1], oacc[b][4 * g + 2], oacc[b][4 * g + 3]};
+        f32x4 x = {oacc[b][4 * g] * f, oacc[b][4 * g + 1] * f, oacc[b][4 * g + 2] * f, oacc[b][4 * g + 3] * f};
         *reinterpret_cast<f32x4*>(os + 32 * b + 8 * g) = x;
       }
   }
@@ -351,12 +378,7 @@ void prefill_bf16_kernel(PrefillParams p) {
 
 template <int D, int QH>
 static hipError_t launch_one(const PrefillParams& p, int grid, hipStream_t stream) {
-  constexpr int smem = 4 * 16384;
-  auto kern = prefill_bf16_kernel<D, QH>;
-  static std::atomic<unsigned> lds_done{0};
-  hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), smem, lds_done);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), smem, stream, p);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, QH>), dim3(grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
