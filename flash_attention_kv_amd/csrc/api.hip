@@ -61,6 +61,28 @@ size_t worklist_capacity(int total, int n_seqs, int BQ) {
   return (size_t)(total / BQ) + (size_t)n_seqs;
 }
 
+// Jagged-batch workspace: [header 256 B: n_items, queue info] [records]
+// and, for bf16, the per-XCD schedule arrays.
+struct JaggedLayout {
+  size_t items, nat2canon, ntprefix, seq_of_rank, sched, total;
+  size_t cap, stride;
+};
+JaggedLayout jagged_layout(int T_q, int n_seqs, int BQ, int n_hg, bool sched) {
+  JaggedLayout L{};
+  L.cap = worklist_capacity(T_q, n_seqs, BQ);
+  L.items = 256;
+  size_t o = L.items + align256(L.cap * FAKV_WORKITEM_BYTES);
+  if (sched) {
+    L.stride = L.cap * (size_t)n_hg;
+    L.nat2canon = o;   o += align256(L.cap * 4);
+    L.ntprefix = o;    o += align256(((size_t)n_seqs + 1) * 4);
+    L.seq_of_rank = o; o += align256((size_t)n_seqs * 4);
+    L.sched = o;       o += align256(8 * L.stride * 4);
+  }
+  L.total = o;
+  return L;
+}
+
 fakv_status check_prefill_common(const void* q, const void* k, const void* v, int h_q, int h_kv,
                                  int d, int dtype) {
   if (!q || !k || !v) return fail(FAKV_EINVAL, "q, k and v must be non-null");
@@ -138,9 +160,11 @@ int fakv_query_tile_rows(int h_q, int h_kv, int d, int dtype) {
 size_t ring_attn_workspace_bytes(int T_q, int S_kv, int h_q, int h_kv, int d, int C, int causal,
                                  int n_seqs, int jagged, int dtype) {
   (void)S_kv; (void)d; (void)C; (void)causal;
-  if (!jagged || T_q <= 0 || h_q < 1 || h_kv < 1 || h_q % h_kv) return 0;
+  if (!jagged || T_q <= 0 || n_seqs < 1 || h_q < 1 || h_kv < 1 || h_q % h_kv) return 0;
   const int BQ = query_tile(h_q, h_kv, dtype);
-  return 256 + align256(worklist_capacity(T_q, n_seqs, BQ) * FAKV_WORKITEM_BYTES);
+  const bool bf16 = dtype == FAKV_BF16;
+  const int n_hg = bf16 ? h_q / heads_per_wg(h_q, h_kv) : h_q;
+  return jagged_layout(T_q, n_seqs, BQ, n_hg, bf16).total;
 }
 
 size_t splitkv_decode_workspace_bytes(int B, int h_q, int d, int n_chunks) {
@@ -243,22 +267,37 @@ fakv_status ring_attn_fwd(const void* q, const void* k, const void* v, void* o, 
   if (workspace == nullptr || workspace_bytes < need)
     return fail(FAKV_EINVAL, "workspace too small: need %zu bytes, got %zu", need, workspace_bytes);
   if (!aligned16(workspace)) return fail(FAKV_EINVAL, "workspace must be 16-byte aligned");
-  const size_t cap = worklist_capacity(T_q, n_seqs, BQ);
-  const long long grid = (long long)cap * (h_q / qh);
-  if (grid > 0x7fffffffll || cap > 0x7fffffffull) return fail(FAKV_EINVAL, "grid too large");
-  int32_t* n_items = static_cast<int32_t*>(workspace);
-  int32_t* items = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + 256);
+  const bool bf16 = dtype == FAKV_BF16;
+  const int n_hg = h_q / qh;
+  const JaggedLayout L = jagged_layout(T_q, n_seqs, BQ, n_hg, bf16);
+  const size_t cap = L.cap;
+  if (cap > 0x7fffffffull || (long long)cap * n_hg > 0x7fffffffll) return fail(FAKV_EINVAL, "grid too large");
+  char* ws = static_cast<char*>(workspace);
+  int32_t* n_items = reinterpret_cast<int32_t*>(ws);
+  int32_t* items = reinterpret_cast<int32_t*>(ws + L.items);
   hipError_t e = fakv::launch_worklist(seq_offsets, n_seqs, T_q, BQ, items, n_items, (int)cap, st);
   if (e != hipSuccess) return device_fail("worklist launch", e);
-  if (grid == 0) return FAKV_OK;
   fakv::PrefillParams p = base_params(q, k, v, h_q, h_kv, d);
   p.o = static_cast<uint16_t*>(o);
   p.mode = 0;
   p.n_seqs = n_seqs; p.T_q = T_q; p.S_kv = S_kv;
   p.C = C; p.causal = causal ? 1 : 0;
   p.items = items; p.n_items = n_items;
-  p.n_hg = h_q / qh;
-  return launch_prefill(p, d, dtype, (int)grid, st);
+  p.n_hg = n_hg;
+  if (!bf16) return launch_prefill(p, d, dtype, (int)(cap * n_hg), st);
+  fakv::SchedBufs sb;
+  sb.qinfo = reinterpret_cast<int32_t*>(ws + 64);
+  sb.nat2canon = reinterpret_cast<int32_t*>(ws + L.nat2canon);
+  sb.ntprefix = reinterpret_cast<int32_t*>(ws + L.ntprefix);
+  sb.seq_of_rank = reinterpret_cast<int32_t*>(ws + L.seq_of_rank);
+  sb.sched = reinterpret_cast<int32_t*>(ws + L.sched);
+  sb.stride = (int)L.stride;
+  e = fakv::launch_schedule(seq_offsets, n_seqs, BQ, items, n_items, n_hg, sb, st);
+  if (e != hipSuccess) return device_fail("schedule launch", e);
+  p.sched = sb.sched;
+  p.sched_stride = sb.stride;
+  p.qinfo = sb.qinfo;
+  return launch_prefill(p, d, dtype, fakv::prefill_bf16_persistent_grid(d, qh), st);
 }
 
 fakv_status splitkv_decode(const void* q, const void* k, const void* v, void* o, int B, int h_q,

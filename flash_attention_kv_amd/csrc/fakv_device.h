@@ -43,8 +43,21 @@ __device__ __forceinline__ f32x16 mfma32x32x2f32(float a, float b, const f32x16&
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-// Value of the other half-wave's lane (l ^ 32).
+// Value of the other half-wave's lane (l ^ 32), through LDS (any wave size).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// max / sum of x over lanes l and l ^ 32 with v_permlane32_swap (a VALU lane
+// swap between the two half-waves, no LDS round trip).  Swapping x with
+// itself leaves, in every lane, one register holding x of lane l mod 32 and
+// the other holding x of lane l mod 32 + 32.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Two fp32 -> two bf16 (round to nearest even, v_cvt_pk_bf16_f32), packed.
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {

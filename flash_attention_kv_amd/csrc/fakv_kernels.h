@@ -26,6 +26,9 @@ struct PrefillParams {
   int q_pos0, k_pos0;
   const int32_t* items;    // jagged worklist records (8 x int32), or nullptr
   const int32_t* n_items;  // device count of records
+  const int32_t* sched;    // bf16 jagged: 8 per-XCD queues of item * n_hg + head group
+  int sched_stride;        // entries reserved per queue
+  int32_t* qinfo;          // queue lengths [0..7] and pop counters [8..15]
   int n_qtiles;            // dense: query tiles per sequence
   int n_hg;                // workgroups per query tile = h_q / heads per workgroup
   float scale;             // 1 / sqrt(d)
@@ -64,5 +67,19 @@ hipError_t launch_decode_partial(const DecodeParams& p, int d, int g, hipStream_
 hipError_t launch_lse_merge(const MergeParams& p, int d, hipStream_t stream);
 hipError_t launch_worklist(const int32_t* seq_offsets, int n_seqs, int total, int BQ,
                            int32_t* items, int32_t* n_items, int capacity, hipStream_t stream);
+
+// Workspace carve-up of the per-XCD schedule built after the worklist.
+struct SchedBufs {
+  int32_t* qinfo;          // 16 ints: queue lengths, pop counters
+  int32_t* nat2canon;      // capacity ints: (seq, tile) in natural order -> record index
+  int32_t* ntprefix;       // n_seqs + 1 ints: prefix sums of tiles per sequence
+  int32_t* seq_of_rank;    // n_seqs ints: sequences sorted by tile count, descending
+  int32_t* sched;          // 8 * stride ints
+  int stride;
+};
+hipError_t launch_schedule(const int32_t* seq_offsets, int n_seqs, int BQ, const int32_t* items,
+                           const int32_t* n_items, int n_hg, const SchedBufs& sb, hipStream_t stream);
+// Resident workgroups of the bf16 prefill kernel on the current device (for persistent grids).
+int prefill_bf16_persistent_grid(int d, int qh);
 
 }  // namespace fakv

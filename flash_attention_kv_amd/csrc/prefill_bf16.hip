@@ -73,9 +73,20 @@ __device__ __forceinline__ bf16x4 tr16(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 __attribute__((address_space(3)))*)(p));
 }
 
+// Geometry of one work item: a query tile [q_lo, q_hi) of one sequence
+// (local indices) and one head group, against that sequence's keys.
+struct ItemGeo {
+  int seq_q0, seq_k0;   // first query / key token of the sequence
+  int Lq, Lk;           // queries / keys of the sequence
+  int q_lo, q_hi;       // query tile
+  int hg;               // head group
+  int jagged;           // chunk width rounds up (jagged) or divides exactly (dense)
+};
+
+// One work item, start to finish: Q rows into registers, the KV walk, the
+// epilogue.  The workgroup's LDS is free on entry and on exit.
 template <int D, int QH>
-__global__ __launch_bounds__(256, 2)
-void prefill_bf16_kernel(PrefillParams p) {
+__device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem, const ItemGeo& g) {
   constexpr int BK = TileK<D>::BK;
   constexpr int WPH = 4 / QH;          // waves per query head
   constexpr int BQ = 32 * WPH;         // query rows per tile
@@ -88,7 +99,6 @@ void prefill_bf16_kernel(PrefillParams p) {
   constexpr int NI = TILE / 16 / 256;  // DMA instructions per thread per tensor
   static_assert(TILE == 16384 && NI == 4, "tile geometry");
 
-  __shared__ __attribute__((aligned(16))) char smem[4 * TILE];  // K0 V0 K1 V1
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -98,52 +108,12 @@ void prefill_bf16_kernel(PrefillParams p) {
   const int half = lane >> 5;
   const int col = lane & 31;
 
-  // ---- work item -----------------------------------------------------------
-  int seq_q0, seq_k0, Lq, Lk, q_lo, q_hi, hg;
-  if (p.items != nullptr) {
-    const int item = blockIdx.x / p.n_hg;
-    hg = blockIdx.x - item * p.n_hg;
-    if (item >= *p.n_items) return;
-    const int32_t* it = p.items + 8 * (size_t)item;
-    seq_q0 = seq_k0 = it[2];
-    Lq = Lk = it[3];
-    q_lo = it[4] - it[2];
-    q_hi = it[6] - it[2];
-  } else {
-    // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs
-    // (workgroup L runs on XCD L % 8).  Group g of (sequence, head-group)
-    // pairs p = 8g .. 8g+7 places pair 8g + x on XCD x, so all query tiles of
-    // one pair -- which read the same K/V -- run on one XCD and share its L2;
-    // within a pair the longest causal tiles go first.
-    const int pairs = p.n_seqs * p.n_hg;
-    const int main_pairs = pairs & ~7;
-    const int L = blockIdx.x;
-    int pair, qr;
-    if (L < main_pairs * p.n_qtiles) {
-      const int slot = L >> 3;
-      const int pl = slot / p.n_qtiles;
-      qr = slot - pl * p.n_qtiles;
-      pair = pl * 8 + (L & 7);
-    } else {
-      const int R = L - main_pairs * p.n_qtiles;
-      const int rp = pairs - main_pairs;
-      qr = R / rp;
-      pair = main_pairs + (R - qr * rp);
-    }
-    const int qt = p.n_qtiles - 1 - qr;
-    const int seq = pair / p.n_hg;
-    hg = pair - seq * p.n_hg;
-    seq_q0 = seq * p.T_q;
-    seq_k0 = seq * p.S_kv;
-    Lq = p.T_q;
-    Lk = p.S_kv;
-    q_lo = qt * BQ;
-    q_hi = min(q_lo + BQ, Lq);
-  }
-  const int head = hg * QH + hl;
+  const int seq_q0 = g.seq_q0, seq_k0 = g.seq_k0, Lq = g.Lq, Lk = g.Lk;
+  const int q_lo = g.q_lo, q_hi = g.q_hi;
+  const int head = g.hg * QH + hl;
   const int kvh = head / (p.h_q / p.h_kv);
   const int delta = p.q_pos0 - p.k_pos0;
-  const int w = (p.items != nullptr) ? (Lk + p.C - 1) / p.C : Lk / p.C;
+  const int w = g.jagged ? (Lk + p.C - 1) / p.C : Lk / p.C;
 
   KvWalk walk;
   walk.S = Lk; walk.C = p.C; walk.w = w;
@@ -291,7 +261,7 @@ void prefill_bf16_kernel(PrefillParams p) {
       for (int b = 0; b < KB; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[b][r]);
-      mt = fmaxf(mt, xor32(mt));
+      mt = halves_max(mt);
       m_true = fmaxf(m_true, mt * scale);
       if (__builtin_amdgcn_ballot_w64(m_true > m_sh + kLazyShift * kLn2) != 0) {
         // move the shift to the true max: rescale by exp(m_sh - m_true)
@@ -344,7 +314,7 @@ void prefill_bf16_kernel(PrefillParams p) {
   }
 
   // ---- epilogue -------------------------------------------------------------
-  float l_tot = l_run + xor32(l_run);
+  float l_tot = halves_sum(l_run);
   if (!qvalid) return;
   if (p.mode == 0) {
     const float inv = 1.f / l_tot;
@@ -377,6 +347,86 @@ void prefill_bf16_kernel(PrefillParams p) {
 }
 
 template <int D, int QH>
+__global__ __launch_bounds__(256, 2)
+void prefill_bf16_kernel(PrefillParams p) {
+  constexpr int BQ = 32 * (4 / QH);
+  __shared__ __attribute__((aligned(16))) char smem[4 * 16384];  // K0 V0 K1 V1
+
+  if (p.sched != nullptr) {
+    // Jagged batch, persistent: pop entries (item * n_hg + head group) from
+    // this XCD's queue -- workgroup L runs on XCD L % 8 -- then steal from
+    // the other queues.  Each queue holds whole (sequence, head group) units,
+    // longest first, so the query tiles that share one sequence's K/V run
+    // together on one XCD and hit its L2.  Every workgroup exits once all
+    // eight queues are drained.
+    __shared__ int s_entry;
+    const int x0 = blockIdx.x & 7;
+    for (;;) {
+      if (threadIdx.x == 0) {
+        int e = -1;
+        for (int q = 0; q < 8 && e < 0; ++q) {
+          const int x = (x0 + q) & 7;
+          const int len = p.qinfo[x];
+          if (__hip_atomic_load(&p.qinfo[8 + x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= len) continue;
+          const int slot = atomicAdd(&p.qinfo[8 + x], 1);
+          if (slot < len) e = p.sched[(size_t)x * p.sched_stride + slot];
+        }
+        s_entry = e;
+      }
+      __syncthreads();
+      const int e = s_entry;
+      __syncthreads();
+      if (e < 0) break;
+      const int item = e / p.n_hg;
+      const int32_t* it = p.items + 8 * (size_t)item;
+      ItemGeo g;
+      g.seq_q0 = g.seq_k0 = it[2];
+      g.Lq = g.Lk = it[3];
+      g.q_lo = it[4] - it[2];
+      g.q_hi = it[6] - it[2];
+      g.hg = e - item * p.n_hg;
+      g.jagged = 1;
+      prefill_item<D, QH>(p, smem, g);
+    }
+    return;
+  }
+
+  // Dense batch, one query tile per workgroup.  XCD-aware order: workgroups
+  // are dispatched round-robin over the 8 XCDs (workgroup L runs on XCD
+  // L % 8).  Group g of (sequence, head-group) pairs p = 8g .. 8g+7 places
+  // pair 8g + x on XCD x, so all query tiles of one pair -- which read the
+  // same K/V -- run on one XCD and share its L2; within a pair the longest
+  // causal tiles go first.
+  const int pairs = p.n_seqs * p.n_hg;
+  const int main_pairs = pairs & ~7;
+  const int L = blockIdx.x;
+  int pair, qr;
+  if (L < main_pairs * p.n_qtiles) {
+    const int slot = L >> 3;
+    const int pl = slot / p.n_qtiles;
+    qr = slot - pl * p.n_qtiles;
+    pair = pl * 8 + (L & 7);
+  } else {
+    const int R = L - main_pairs * p.n_qtiles;
+    const int rp = pairs - main_pairs;
+    qr = R / rp;
+    pair = main_pairs + (R - qr * rp);
+  }
+  const int qt = p.n_qtiles - 1 - qr;
+  const int seq = pair / p.n_hg;
+  ItemGeo g;
+  g.hg = pair - seq * p.n_hg;
+  g.seq_q0 = seq * p.T_q;
+  g.seq_k0 = seq * p.S_kv;
+  g.Lq = p.T_q;
+  g.Lk = p.S_kv;
+  g.q_lo = qt * BQ;
+  g.q_hi = min(g.q_lo + BQ, g.Lq);
+  g.jagged = 0;
+  prefill_item<D, QH>(p, smem, g);
+}
+
+template <int D, int QH>
 static hipError_t launch_one(const PrefillParams& p, int grid, hipStream_t stream) {
   hipLaunchKernelGGL((prefill_bf16_kernel<D, QH>), dim3(grid), dim3(256), 0, stream, p);
   return hipGetLastError();
@@ -393,6 +443,39 @@ static hipError_t launch_qh(const PrefillParams& p, int qh, int grid, hipStream_
 }
 
 int prefill_bf16_block_k(int d) { return 8192 / d; }
+
+template <int D, int QH>
+static int resident_per_cu() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_bf16_kernel<D, QH>, 256, 0) != hipSuccess) n = 1;
+  return n > 0 ? n : 1;
+}
+
+int prefill_bf16_persistent_grid(int d, int qh) {
+  static std::atomic<int> cache[32][9];   // per device, per (d, qh)
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  const int key = (d == 64 ? 0 : d == 128 ? 3 : 6) + (qh == 1 ? 0 : qh == 2 ? 1 : 2);
+  int g = cache[dev & 31][key].load(std::memory_order_relaxed);
+  if (g > 0) return g;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  int per = 1;
+  switch (key) {
+    case 0: per = resident_per_cu<64, 1>(); break;
+    case 1: per = resident_per_cu<64, 2>(); break;
+    case 2: per = resident_per_cu<64, 4>(); break;
+    case 3: per = resident_per_cu<128, 1>(); break;
+    case 4: per = resident_per_cu<128, 2>(); break;
+    case 5: per = resident_per_cu<128, 4>(); break;
+    case 6: per = resident_per_cu<256, 1>(); break;
+    case 7: per = resident_per_cu<256, 2>(); break;
+    default: per = resident_per_cu<256, 4>(); break;
+  }
+  g = per * cus;
+  cache[dev & 31][key].store(g, std::memory_order_relaxed);
+  return g;
+}
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, int d, int qh, int grid, hipStream_t stream) {
   switch (d) {

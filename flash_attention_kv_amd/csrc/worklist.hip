@@ -77,6 +77,127 @@ void worklist_kernel(const int32_t* __restrict__ off, int n_seqs, int total, int
   if (tid == 0) *n_items = min(base, capacity);
 }
 
+// ---------------------------------------------------------------------------
+// Per-XCD schedule of a jagged batch (bf16 prefill).  Units are
+// (sequence, head group) pairs; sequences are ranked by tile count, longest
+// first, and the units of that order are dealt round-robin onto 8 queues
+// (unit k -> queue k mod 8).  A unit's entries -- its query tiles, longest
+// first -- are contiguous in its queue, so the workgroups that pop them run
+// at the same time on one XCD and share that sequence's K/V in its L2.
+// Entry = record index * n_hg + head group.  Runs after worklist_kernel on
+// the same stream; an empty worklist gives empty queues.
+__global__ __launch_bounds__(1024)
+void schedule_kernel(const int32_t* __restrict__ off, int n_seqs, int BQ, const int32_t* __restrict__ items,
+                     const int32_t* __restrict__ n_items_p, int n_hg, SchedBufs sb) {
+  __shared__ int s_val[1024];
+  __shared__ int s_wave[16];
+  __shared__ int s_carry[8];
+  __shared__ int s_misc[2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n_items = *n_items_p;
+  if (n_items == 0) {          // empty batch or rejected offsets
+    if (tid < 16) sb.qinfo[tid] = 0;
+    return;
+  }
+  // (offsets are a valid prefix array here: worklist_kernel checked them)
+  auto ntiles = [&](int b) { return (off[b + 1] - off[b] + BQ - 1) / BQ; };
+
+  // 1. exclusive prefix sums of tiles per sequence
+  if (tid == 0) { s_misc[0] = 0; s_misc[1] = 0; }
+  __syncthreads();
+  for (int b0 = 0; b0 < n_seqs; b0 += 1024) {
+    const int b = b0 + tid;
+    const int v = b < n_seqs ? ntiles(b) : 0;
+    s_val[tid] = v;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {
+      const int t = tid >= d ? s_val[tid - d] : 0;
+      __syncthreads();
+      s_val[tid] += t;
+      __syncthreads();
+    }
+    if (b < n_seqs) sb.ntprefix[b] = s_misc[0] + s_val[tid] - v;
+    atomicMax(&s_misc[1], v);
+    __syncthreads();
+    if (tid == 1023) s_misc[0] += s_val[1023];
+    __syncthreads();
+  }
+  if (tid == 0) sb.ntprefix[n_seqs] = s_misc[0];
+  const int T = s_misc[1];
+  __syncthreads();
+
+  // 2. (sequence, tile) in natural order -> worklist record index
+  for (int i = tid; i < n_items; i += 1024) {
+    const int32_t* r = items + 8 * (size_t)i;
+    sb.nat2canon[sb.ntprefix[r[0]] + r[1]] = i;
+  }
+
+  // 3. rank sequences by tile count, descending, ties by index
+  int base = 0;
+  for (int v = T; v >= 1; --v) {
+    for (int b0 = 0; b0 < n_seqs; b0 += 1024) {
+      const int b = b0 + tid;
+      const bool flag = b < n_seqs && ntiles(b) == v;
+      const unsigned long long bal = __ballot(flag);
+      const int below = __popcll(bal & ((1ull << lane) - 1ull));
+      if (lane == 0) s_wave[wave] = __popcll(bal);
+      __syncthreads();
+      int pre = 0, tot = 0;
+      for (int w = 0; w < 16; ++w) {
+        const int c = s_wave[w];
+        pre += (w < wave) ? c : 0;
+        tot += c;
+      }
+      if (flag) sb.seq_of_rank[base + pre + below] = b;
+      base += tot;
+      __syncthreads();
+    }
+  }
+  const int n_units = base * n_hg;     // non-empty sequences x head groups
+  __syncthreads();                     // seq_of_rank and nat2canon complete
+
+  // 4. deal units onto the queues; per-queue offsets by a stride-8 scan
+  if (tid < 8) s_carry[tid] = 0;
+  __syncthreads();
+  for (int k0 = 0; k0 < n_units; k0 += 1024) {
+    const int k = k0 + tid;
+    const bool valid = k < n_units;
+    const int r = valid ? k / n_hg : 0;
+    const int hg = valid ? k - r * n_hg : 0;
+    const int b = valid ? sb.seq_of_rank[r] : 0;
+    const int v = valid ? ntiles(b) : 0;
+    const int x = tid & 7;             // == k mod 8 since k0 is a multiple of 1024
+    s_val[tid] = v;
+    __syncthreads();
+    for (int d = 8; d < 1024; d <<= 1) {
+      const int t = tid >= d ? s_val[tid - d] : 0;
+      __syncthreads();
+      s_val[tid] += t;
+      __syncthreads();
+    }
+    if (valid) {
+      const int pos = s_carry[x] + s_val[tid] - v;
+      int32_t* q = sb.sched + (size_t)x * sb.stride + pos;
+      const int32_t* nc = sb.nat2canon + sb.ntprefix[b];
+      for (int j = 0; j < v; ++j) q[j] = nc[v - 1 - j] * n_hg + hg;
+    }
+    __syncthreads();
+    if (tid >= 1016) s_carry[x] += s_val[tid];
+    __syncthreads();
+  }
+  if (tid < 8) {
+    sb.qinfo[tid] = s_carry[tid];
+    sb.qinfo[8 + tid] = 0;
+  }
+}
+
+hipError_t launch_schedule(const int32_t* seq_offsets, int n_seqs, int BQ, const int32_t* items,
+                           const int32_t* n_items, int n_hg, const SchedBufs& sb, hipStream_t stream) {
+  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, stream, seq_offsets, n_seqs, BQ, items,
+                     n_items, n_hg, sb);
+  return hipGetLastError();
+}
+
 hipError_t launch_worklist(const int32_t* seq_offsets, int n_seqs, int total, int BQ,
                            int32_t* items, int32_t* n_items, int capacity, hipStream_t stream) {
   hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(1024), 0, stream, seq_offsets, n_seqs, total,
