@@ -314,6 +314,8 @@ fakv_status splitkv_decode(const void* q, const void* k, const void* v, void* o,
     return fail(FAKV_EINVAL, "need 1 <= n_chunks <= S_kv (got %d)", n_chunks);
   if (h_q / h_kv > 32) return fail(FAKV_EUNSUPPORTED, "GQA group h_q/h_kv = %d exceeds 32", h_q / h_kv);
   if ((long long)B * S_kv * h_kv * d >= (1ll << 40)) return fail(FAKV_EINVAL, "tensor too large");
+  if ((long long)B * h_q >= (1ll << 31)) return fail(FAKV_EINVAL, "B * h_q exceeds int32");
+  if ((s = check_kv_extent(S_kv, h_kv, d, dtype)) != FAKV_OK) return s;
   if ((long long)B * h_kv * n_chunks > 0x7fffffffll) return fail(FAKV_EINVAL, "grid too large");
   const size_t need = splitkv_decode_workspace_bytes(B, h_q, d, n_chunks);
   if (workspace == nullptr || workspace_bytes < need)

@@ -8,47 +8,51 @@
 // query heads of the group at once, so every K/V byte is read from HBM once.
 // The g query heads are the 32 columns of the MFMA (columns >= g are zero).
 //
-// The path is bandwidth-bound (8 FLOP per byte).  Each of the 4 waves streams
-// its own contiguous quarter of the chunk in steps of 32 keys, with the next
-// step's loads in flight while the current one computes; there is no
-// workgroup barrier in the streaming loop:
-//   K: each lane loads its key row's dims straight into the MFMA A operand
-//      (S^T = K Q^T needs key rows, which is how K is stored);
-//   V: lanes load 16-byte row chunks, transpose 4 keys x 8 dims in registers
-//      and pass them through a wave-private LDS slab in the quad layout, from
-//      which the A operand of O^T += V^T P^T is read.
-// At the end the 4 waves' triplets merge (online-softmax rule) through LDS
-// and wave 0 writes the chunk's triplet: m, l (n_chunks, B*h_q) and
-// O unnormalised (n_chunks, B*h_q, d), the layout lse_merge consumes.
+// The path is bandwidth-bound (8 FLOP per byte).  Each wave owns one whole
+// (sequence, KV head, chunk) unit -- a workgroup holds four -- and streams it
+// in steps of 32 keys, two steps in flight, with no barrier anywhere:
+//   K: each lane loads its key row's dims straight into the MFMA A operand of
+//      S^T = K Q^T (key rows are how K is stored), double-buffered registers;
+//   V: 32 x d tiles go HBM -> LDS directly (buffer_load ... lds) into two
+//      wave-private stages, swizzled so that the A operand of O^T += V^T P^T
+//      is read with the conflict-free transpose read ds_read_b64_tr_b16.
+// Buffer resources span one (sequence, KV head)'s keys, so no load can leave
+// the cache tensors.  Each wave writes its unit's triplet: m, l
+// (n_chunks, B*h_q) and O unnormalised (n_chunks, B*h_q, d), the layout
+// lse_merge consumes.
+#include <type_traits>
+#include <utility>
+
 #include "fakv_device.h"
 #include "fakv_kernels.h"
 
 namespace fakv {
 
 template <int D>
-__global__ __launch_bounds__(256, 1)
+__global__ __launch_bounds__(256, 2)
 void decode_partial_kernel(DecodeParams p, int g) {
   constexpr int DS = D / 16;
   constexpr int DB = D / 32;
   constexpr int NCH = D / 8;                 // 16-byte chunks per key row
-  constexpr int VTASK = 8 * NCH / 64;        // (quad, chunk) tasks per lane per 32-key step
-  constexpr int SLAB = 32 * D * 2;           // bytes of one wave's V slab
-  static_assert(VTASK * 64 == 8 * NCH, "V tasks must divide over the wave");
+  constexpr int STAGE = 32 * D * 2;          // bytes of one 32-key V stage
+  constexpr int NV = 32 * NCH / 64;          // V loads per lane per step
+  constexpr int NVA = DB < 4 ? DB : 4;
+  constexpr int NKB = D <= 128 ? 2 : 1;      // K register buffers
+  __shared__ __attribute__((aligned(16))) char smem[4 * 2 * STAGE];
 
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
-  const int c = blockIdx.x % p.n_chunks;
-  const int kvh = (blockIdx.x / p.n_chunks) % p.h_kv;
-  const int b = blockIdx.x / (p.n_chunks * p.h_kv);
+  // unit = (sequence, chunk, KV head), KV head fastest: the waves of a
+  // workgroup stream neighbouring head slices of the same token rows
+  const int unit = blockIdx.x * 4 + wave;
+  if (unit >= p.B * p.h_kv * p.n_chunks) return;
+  const int kvh = unit % p.h_kv;
+  const int c = (unit / p.h_kv) % p.n_chunks;
+  const int b = unit / (p.n_chunks * p.h_kv);
 
-  const int c0 = min(c * p.chunk_w, p.S);
-  const int c1 = min(c0 + p.chunk_w, p.S);
-  const int n = c1 - c0;
-  const int per = ((n + 127) / 128) * 32;    // keys per wave, a multiple of 32
-  const int w0 = min(c0 + wave * per, c1);
-  const int w1 = min(w0 + per, c1);
+  const int w0 = min(c * p.chunk_w, p.S);
+  const int w1 = min(w0 + p.chunk_w, p.S);
   const int nsteps = (w1 - w0 + 31) / 32;
 
   // query heads of the group as B operands (column col = head kvh*g + col)
@@ -65,54 +69,56 @@ void decode_partial_kernel(DecodeParams p, int g) {
     }
   }
 
-  const size_t kv_stride = (size_t)p.h_kv * D;
-  const uint16_t* kbase = p.k + ((size_t)b * p.S * p.h_kv + kvh) * D;
-  const uint16_t* vbase = p.v + ((size_t)b * p.S * p.h_kv + kvh) * D;
-  char* slab = smem + wave * SLAB;
+  const unsigned stride_b = (unsigned)p.h_kv * D * 2;
+  const size_t head_off = ((size_t)b * p.S * p.h_kv + kvh) * D;
+  const unsigned extent = (unsigned)(p.S - 1) * stride_b + D * 2;
+  const __amdgpu_buffer_rsrc_t rs_k = make_rsrc(p.k + head_off, extent);
+  const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(p.v + head_off, extent);
+  char* wl = smem + wave * 2 * STAGE;       // this wave's two V stages
+
+  // V stage slot l of load i holds row (64 i + l) / NCH, physical chunk (..) % NCH
+  unsigned voff_v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int sl = 64 * i + lane;
+    const int r = sl / NCH, pc = sl % NCH;
+    voff_v[i] = (unsigned)r * stride_b + (unsigned)((pc ^ vmask<D>(r)) * 16);
+  }
+  const unsigned koff = (unsigned)col * stride_b + 16u * half;   // + 32 s bytes
+  const lds_char* vaddr[NVA];
+  {
+    const int vg16 = (lane >> 4) & 1, vp = lane & 15;
+    const int vrow = 4 * half + (vp >> 2);
+    const int vmsk = vmask<D>(vrow);
+#pragma unroll
+    for (int i = 0; i < NVA; ++i)
+      vaddr[i] = (const lds_char*)(wl) + vrow * (D * 2) + ((4 * i + 2 * vg16 + ((vp & 3) >> 1)) ^ vmsk) * 16 +
+                 (vp & 1) * 8;
+  }
+
+  u32x4 kr[NKB][DS];
+  auto issue_k = [&](int k0, int slot) {
+#pragma unroll
+    for (int s = 0; s < DS; ++s)
+      kr[slot][s] = __builtin_amdgcn_raw_buffer_load_b128(rs_k, (int)((unsigned)k0 * stride_b + koff + 32u * s), 0, 0);
+  };
+  auto issue_v = [&](int k0, int stage) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) dma16(rs_v, (unsigned)k0 * stride_b + voff_v[i], wl + stage * STAGE + 1024 * i);
+  };
 
   f32x16 oacc[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
   float m_run = neg_inf(), l_run = 0.f;
 
-  struct Regs { u32x4 k[DS]; u32x4 v[VTASK][4]; };
-  auto load = [&](int k0, Regs& R) {
-    const int kr = k0 + col;
-#pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (kr < w1) x = *reinterpret_cast<const u32x4*>(kbase + (size_t)kr * kv_stride + 16 * s + 8 * half);
-      R.k[s] = x;
-    }
-#pragma unroll
-    for (int t = 0; t < VTASK; ++t) {
-      const int id = lane + 64 * t;
-      const int kq = id / NCH, ch = id % NCH;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = k0 + 4 * kq + j;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (r < w1) x = *reinterpret_cast<const u32x4*>(vbase + (size_t)r * kv_stride + 8 * ch);
-        R.v[t][j] = x;
-      }
-    }
-  };
-  auto process = [&](int k0, const Regs& R) {
-    // V -> wave slab (quad layout)
-#pragma unroll
-    for (int t = 0; t < VTASK; ++t) {
-      const int id = lane + 64 * t;
-      const int kq = id / NCH, ch = id % NCH;
-      u32x4 o4[4];
-      quad_transpose(R.v[t], o4);
-      char* dst = slab + (kq * D + 8 * ch) * 8;
-#pragma unroll
-      for (int pc = 0; pc < 4; ++pc) *reinterpret_cast<u32x4*>(dst + 16 * pc) = o4[pc];
-    }
+  auto process = [&](int k0, auto stc) {
+    constexpr int ST = decltype(stc)::value;
     // S^T = K Q^T (32 keys x 32 columns)
     f32x16 sacc = f32x16{};
 #pragma unroll
-    for (int s = 0; s < DS; ++s) sacc = mfma32x32x16(__builtin_bit_cast(bf16x8, R.k[s]), qreg[s], sacc);
+    for (int s = 0; s < DS; ++s)
+      sacc = mfma32x32x16(__builtin_bit_cast(bf16x8, kr[NKB == 2 ? ST : 0][s]), qreg[s], sacc);
     if (k0 + 32 > w1) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -123,89 +129,87 @@ void decode_partial_kernel(DecodeParams p, int g) {
     float mt = neg_inf();
 #pragma unroll
     for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[r]);
-    mt = fmaxf(mt, xor32(mt));
+    mt = halves_max(mt);
     const float m_new = fmaxf(m_run, mt * p.scale);
     const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
-    const float alpha = fast_exp2((m_run - m_use) * kLog2e);
     const float mlog = m_use * kLog2e;
-    float rs = 0.f;
+    if (__builtin_amdgcn_ballot_w64(m_new != m_run) != 0) {
+      const float alpha = fast_exp2((m_run - m_use) * kLog2e);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+    }
+    m_run = m_new;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float e = fast_exp2(__builtin_fmaf(sacc[r], p.scale_log2, -mlog));
       sacc[r] = e;
-      rs += e;
+      l_run += e;
     }
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < DB; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    // O^T += V^T P^T from this step's V stage
+    static_for<2>([&](auto ksc) {
+      constexpr int ks = decltype(ksc)::value;
       float pv[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) pv[j] = sacc[8 * ks + j];
       const bf16x8 pb = pack_bf16x8(pv);
-      const char* q0 = slab + ((4 * ks + half) * D) * 8;
-      const char* q1 = slab + ((4 * ks + 2 + half) * D) * 8;
+      static_for<DB / NVA>([&](auto gc) {
+        constexpr int G = decltype(gc)::value;
+        constexpr int OFF = ST * STAGE + 16 * ks * (D * 2) + G * 256;
+        u32x2 lo[NVA], hi[NVA];
 #pragma unroll
-      for (int i = 0; i < DB; ++i) {
-        const int e = 32 * i + col;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(q0 + e * 8);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(q1 + e * 8);
-        const u32x4 a4 = {lo[0], lo[1], hi[0], hi[1]};
-        oacc[i] = mfma32x32x16(__builtin_bit_cast(bf16x8, a4), pb, oacc[i]);
-      }
-    }
+        for (int i = 0; i < NVA; ++i) {
+          lo[i] = tr16_at<OFF>(vaddr[i]);
+          hi[i] = tr16_at<OFF + 8 * (D * 2)>(vaddr[i]);
+        }
+        lds_wait();
+#pragma unroll
+        for (int i = 0; i < NVA; ++i) {
+          lds_ready(lo[i]);
+          lds_ready(hi[i]);
+          const u32x4 a4 = {lo[i][0], lo[i][1], hi[i][0], hi[i][1]};
+          oacc[G * NVA + i] = mfma32x32x16(__builtin_bit_cast(bf16x8, a4), pb, oacc[G * NVA + i]);
+        }
+      });
+    });
   };
 
-  Regs A, Bv;
-  if (nsteps > 0) load(w0, A);
+  // Step st uses K buffer st % NKB and V stage st % 2.  Loads of step st + 2
+  // (st + 1 with one K buffer) are issued as soon as their buffer is free.
+  // The loads are issued unconditionally -- past the wave's range they hit
+  // offsets beyond the resource (read as zero) or other waves' keys, and are
+  // never used -- so every step sees the same number of younger loads in
+  // flight and the waits below are exact.
+  issue_k(w0, 0);
+  issue_v(w0, 0);
+  if (NKB == 2) issue_k(w0 + 32, 1);
+  issue_v(w0 + 32, 1);
+  auto step = [&](int st, auto stc) {
+    constexpr int ST = decltype(stc)::value;
+    const int k0 = w0 + 32 * st;
+    // this step's loads have landed once only the next step's are pending
+    vm_wait<(NKB == 2 ? DS : 0) + NV>();
+    process(k0, stc);
+    if (NKB == 1) issue_k(k0 + 32, 0);
+    if (NKB == 2) issue_k(k0 + 64, ST);
+    issue_v(k0 + 64, ST);
+  };
   for (int st = 0; st < nsteps; st += 2) {
-    if (st + 1 < nsteps) load(w0 + 32 * (st + 1), Bv);
-    process(w0 + 32 * st, A);
-    if (st + 1 < nsteps) {
-      if (st + 2 < nsteps) load(w0 + 32 * (st + 2), A);
-      process(w0 + 32 * (st + 1), Bv);
-    }
+    step(st, std::integral_constant<int, 0>{});
+    if (st + 1 < nsteps) step(st + 1, std::integral_constant<int, 1>{});
   }
 
-  // ---- merge the 4 waves' triplets (fixed order 0 <- 1 <- 2 <- 3) ----------
-  const float l_tot = l_run + xor32(l_run);
-  __syncthreads();                              // slabs are free from here on
-  float* red = reinterpret_cast<float*>(smem);  // [wave][col][D + 2]
-  constexpr int RS = D + 2;
-  if (wave > 0) {
-    float* dst = red + ((wave - 1) * 32 + col) * RS;
-    if (half == 0) { dst[D] = m_run; dst[D + 1] = l_tot; }
-#pragma unroll
-    for (int i = 0; i < DB; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dst[32 * i + 8 * (r >> 2) + 4 * half + (r & 3)] = oacc[i][r];
-  }
-  __syncthreads();
-  if (wave != 0 || !cvalid) return;
-  float m = m_run, l = l_tot;
-  for (int wv = 1; wv < 4; ++wv) {
-    const float* src = red + ((wv - 1) * 32 + col) * RS;
-    const float m2 = src[D], l2 = src[D + 1];
-    const float mn = fmaxf(m, m2);
-    const float mu = (mn == neg_inf()) ? 0.f : mn;
-    const float a1 = fast_exp2((m - mu) * kLog2e), a2 = fast_exp2((m2 - mu) * kLog2e);
-    l = l * a1 + l2 * a2;
-    m = mn;
-#pragma unroll
-    for (int i = 0; i < DB; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        oacc[i][r] = oacc[i][r] * a1 + src[32 * i + 8 * (r >> 2) + 4 * half + (r & 3)] * a2;
-  }
+  // ---- this unit's triplet -------------------------------------------------
+  const float l_tot = halves_sum(l_run);
+  vm_wait<0>();                 // no load into LDS may still be in flight at exit
+  if (!cvalid) return;
   const size_t row = (size_t)b * p.h_q + head;
   const size_t rows = (size_t)p.B * p.h_q;
   if (half == 0) {
-    p.m_parts[(size_t)c * rows + row] = m;
-    p.l_parts[(size_t)c * rows + row] = l;
+    p.m_parts[(size_t)c * rows + row] = m_run;
+    p.l_parts[(size_t)c * rows + row] = l_tot;
   }
   float* op = p.o_parts + ((size_t)c * rows + row) * D + 4 * half;
 #pragma unroll
@@ -219,15 +223,9 @@ void decode_partial_kernel(DecodeParams p, int g) {
 
 template <int D>
 static hipError_t launch_decode(const DecodeParams& p, int g, hipStream_t stream) {
-  constexpr int slabs = 4 * 32 * D * 2;
-  constexpr int red = 3 * 32 * (D + 2) * 4;
-  constexpr int smem = slabs > red ? slabs : red;
-  static std::atomic<unsigned> lds_done{0};
-  auto kern = decode_partial_kernel<D>;
-  hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), smem, lds_done);
-  if (e != hipSuccess) return e;
-  const long long grid = (long long)p.B * p.h_kv * p.n_chunks;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), smem, stream, p, g);
+  const long long units = (long long)p.B * p.h_kv * p.n_chunks;
+  const long long grid = (units + 3) / 4;
+  hipLaunchKernelGGL(decode_partial_kernel<D>, dim3((unsigned)grid), dim3(256), 0, stream, p, g);
   return hipGetLastError();
 }
 

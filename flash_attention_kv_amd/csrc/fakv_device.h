@@ -16,6 +16,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace fakv {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -79,32 +82,67 @@ template <typename T>
 __device__ __forceinline__ T ldg(const T* p) { return *p; }
 
 // ---------------------------------------------------------------------------
-// K tile in LDS: row = one key (D bf16 = D/8 chunks of 16 B).  Chunk c of row
-// r lives at chunk position c ^ f(r), so the 32 lanes of an A-operand read
-// (32 consecutive keys, one chunk) hit distinct 16-byte bank groups.
-template <int D>
-__device__ __forceinline__ int kswz(int r, int c) {
-  if constexpr (D == 64) return c ^ (r & 7);
-  else return c ^ (r & 15);
+// ---------------------------------------------------------------------------
+// Buffer resources and direct HBM -> LDS loads.
+
+// Raw buffer over `bytes` bytes at `base` (gfx9 dword3: 32-bit untyped data).
+// Loads at or past `bytes` return 0, so a resource bounds every access made
+// through it.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// V tile in LDS, "quad-transposed": for every group of 4 consecutive keys
-// (a quad) and every dimension e, the 4 bf16 values V[4q .. 4q+3][e] are
-// stored together (8 bytes) at byte offset (q * D + e) * 8.  An A-operand read
-// of V^T then takes two 8-byte loads per lane (keys 4h..4h+3 and 8+4h..8+4h+3
-// of a 16-key step), and 32 lanes read 32 consecutive dimensions.
-//
-// Transpose 4 keys x 8 dims (4 x 16-byte chunks, one per key) into the quad
-// layout: out[p] holds dims 2p and 2p+1, each as (keys 0-1, keys 2-3).
-__device__ __forceinline__ void quad_transpose(const u32x4 in[4], u32x4 out[4]) {
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    unsigned a = in[0][p], b = in[1][p], c = in[2][p], d = in[3][p];
-    out[p][0] = (a & 0xffffu) | (b << 16);          // dim 2p,   keys 0,1
-    out[p][1] = (c & 0xffffu) | (d << 16);          // dim 2p,   keys 2,3
-    out[p][2] = (a >> 16) | (b & 0xffff0000u);      // dim 2p+1, keys 0,1
-    out[p][3] = (c >> 16) | (d & 0xffff0000u);      // dim 2p+1, keys 2,3
-  }
+// One 16-byte load per lane from a buffer resource straight into LDS; lane l
+// writes lds_wave_base + 16 l.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, unsigned voff, char* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_wave_base, 16,
+                                           voff, 0, 0, 0);
+}
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+// LDS transpose read ds_read_b64_tr_b16 at p + OFF, issued as inline asm so
+// that outstanding HBM -> LDS loads into other buffers are not waited for
+// (the compiler treats its builtin form as touching any LDS byte).  Call
+// lds_wait() and then lds_ready() on the results before using them.
+template <int OFF>
+__device__ __forceinline__ u32x2 tr16_at(const lds_char* p) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(p), "i"(OFF));
+  return r;
+}
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// Ties a value to the preceding lds_wait() so no use is scheduled above it.
+__device__ __forceinline__ void lds_ready(u32x2& x) { asm volatile("" : "+v"(x)); }
+
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(std::integral_constant<int, i>) for i = 0 .. N-1: each index a compile-time constant.
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Wait until at most N vector-memory loads of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory"); }
+
+// ---------------------------------------------------------------------------
+// Chunk swizzles.  K: chunk c of row r at c ^ (r & 15) (c ^ (r & 7) for
+// d = 64): the 16 lanes of each ds_read_b128 pass read 16 consecutive keys at
+// one chunk and hit 16 distinct 16-byte bank groups.  V: rows r .. r+3 read by
+// one half-wave in a transpose read land in distinct 64-byte bank groups.
+template <int D>
+__device__ __forceinline__ int vmask(int r) {
+  if constexpr (D == 64) return ((r >> 1) & 1) << 2;
+  else return (r & 3) << 2;
+}
+template <int D>
+__device__ __forceinline__ int kmask(int r) {
+  if constexpr (D == 64) return r & 7;
+  else return r & 15;
 }
 
 // ---------------------------------------------------------------------------

@@ -5,12 +5,17 @@
 // every part is rescaled by exp(m_c - m') and the l's and O's add.  Applied to
 // all n parts of a row at once it reads: m' = max_c m_c, l' = sum_c l_c
 // exp(m_c - m'), O' = sum_c O_c exp(m_c - m') -- the root of a one-level merge
-// tree, equal in exact arithmetic to any pairwise order.  Sums run in part
-// order c = 0 .. n-1, so results are reproducible bit for bit.  Parts with
+// tree, equal in exact arithmetic to any pairwise order.  Parts with
 // m = -inf (empty chunks) get weight 0.
 //
-// Threads: one per (row, 4 consecutive dims); a row's threads read its parts'
-// m / l redundantly (cached) and their own 16-byte slice of each O part.
+// One workgroup per row: thread t owns 4 consecutive dims (t mod D/4) of the
+// parts c = g, g + G, g + 2G, ... of part group g = t / (D/4), G = 1024/D.
+// The common max comes from an LDS max over the groups; each group sums its
+// parts in order, then the G group sums are added in group order -- a fixed
+// order, so results are reproducible bit for bit.
+#include <type_traits>
+#include <utility>
+
 #include "fakv_device.h"
 #include "fakv_kernels.h"
 
@@ -19,25 +24,44 @@ namespace fakv {
 template <int D>
 __global__ __launch_bounds__(256)
 void lse_merge_kernel(MergeParams p) {
-  constexpr int TPR = D / 4;               // threads per row
-  constexpr int RPB = 256 / TPR;           // rows per block
+  constexpr int TPR = D / 4;               // threads per part group
+  constexpr int G = 256 / TPR;             // part groups
+  __shared__ float s_m[G];
+  __shared__ f32x4 s_o[G][TPR];
+  __shared__ float s_l[G];
   const int t = threadIdx.x % TPR;
-  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
-  if (row >= p.rows) return;
+  const int grp = threadIdx.x / TPR;
+  const size_t row = blockIdx.x;
   const size_t rows = (size_t)p.rows;
 
   float M = neg_inf();
-  for (int c = 0; c < p.n_parts; ++c) M = fmaxf(M, p.m_parts[(size_t)c * rows + row]);
+  for (int c = grp; c < p.n_parts; c += G) M = fmaxf(M, p.m_parts[(size_t)c * rows + row]);
+  if (t == 0) s_m[grp] = M;
+  __syncthreads();
+  M = s_m[0];
+#pragma unroll
+  for (int q = 1; q < G; ++q) M = fmaxf(M, s_m[q]);
   const float Mu = (M == neg_inf()) ? 0.f : M;
 
   float l = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  for (int c = 0; c < p.n_parts; ++c) {
+  for (int c = grp; c < p.n_parts; c += G) {
     const size_t idx = (size_t)c * rows + row;
     const float wgt = fast_exp2((p.m_parts[idx] - Mu) * kLog2e);
     l += wgt * p.l_parts[idx];
     const f32x4 x = *reinterpret_cast<const f32x4*>(p.o_parts + idx * D + 4 * t);
     o += wgt * x;
+  }
+  s_o[grp][t] = o;
+  if (t == 0) s_l[grp] = l;
+  __syncthreads();
+  if (grp != 0) return;
+  l = s_l[0];
+  o = s_o[0][t];
+#pragma unroll
+  for (int q = 1; q < G; ++q) {
+    l += s_l[q];
+    o += s_o[q][t];
   }
   const float inv = 1.f / l;
   if (p.out_bf16) {
@@ -51,10 +75,8 @@ void lse_merge_kernel(MergeParams p) {
 
 template <int D>
 static hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
-  constexpr int RPB = 256 / (D / 4);
-  const long long grid = ((long long)p.rows + RPB - 1) / RPB;
-  if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(lse_merge_kernel<D>, dim3((unsigned)grid), dim3(256), 0, stream, p);
+  if (p.rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(lse_merge_kernel<D>, dim3((unsigned)p.rows), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

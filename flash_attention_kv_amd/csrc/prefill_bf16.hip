@@ -37,33 +37,6 @@ constexpr float kLazyShift = 8.f;
 // Keys per tile by head dim: every K or V tile is 1024 16-byte slots (16 KB).
 template <int D> struct TileK { static constexpr int BK = 8192 / D; };
 
-// Chunk swizzles.  K: chunk c of row r at c ^ (r & 15) (c ^ (r & 7) for
-// d = 64): the 16 lanes of each ds_read_b128 pass read 16 consecutive keys at
-// one chunk and hit 16 distinct 16-byte bank groups.  V: rows r .. r+3 read by
-// one half-wave in a transpose read land in distinct 64-byte bank groups.
-template <int D>
-__device__ __forceinline__ int vmask(int r) {
-  if constexpr (D == 64) return ((r >> 1) & 1) << 2;
-  else return (r & 3) << 2;
-}
-template <int D>
-__device__ __forceinline__ int kmask(int r) {
-  if constexpr (D == 64) return r & 7;
-  else return r & 15;
-}
-
-// One 16-byte load per lane from a buffer resource straight into LDS; lane l
-// writes lds_wave_base + 16 l.  Offsets at or past the resource's size read 0.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, unsigned voff, char* lds_wave_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_wave_base, 16,
-                                           voff, 0, 0, 0);
-}
-
-// Raw buffer over `bytes` bytes at `base` (gfx9 dword3: 32-bit untyped data).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
 __device__ __forceinline__ void wait_dma_and_sync() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();

@@ -93,9 +93,9 @@ fakv_status attn_partial(const void* q, const void* k, const void* v,
  * m_parts, l_parts: (n_parts, rows) fp32; o_parts: (n_parts, rows, d) fp32
  * (unnormalised O).  Per row the online-softmax merge is applied to all parts
  * at once: the common max m' = max_c m_c first, then every part is rescaled by
- * exp(m_c - m') and the l's and O's are summed in part order c = 0..n-1 (a
- * part with m = -inf weighs 0).  Then O / l is written to o_out (rows, d) in
- * out_dtype, and
+ * exp(m_c - m') and the l's and O's are summed in a fixed order (a part with
+ * m = -inf weighs 0), so results are reproducible.  Then O / l is written to
+ * o_out (rows, d) in out_dtype, and
  * m + ln l to lse_out (rows) unless lse_out is NULL.  A row whose merged l is
  * 0 (every part empty) yields NaN output; callers never produce one.
  * This is the merge of the decode page's per-rank triplets and of the prefill
