@@ -111,9 +111,23 @@ __device__ __forceinline__ u32x2 tr16_at(const lds_char* p) {
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(p), "i"(OFF));
   return r;
 }
+// 16-byte LDS read at p + OFF, inline asm for the same reason.
+template <int OFF>
+__device__ __forceinline__ u32x4 ds_read16_at(const lds_char* p) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(p), "i"(OFF));
+  return r;
+}
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// Wait until at most N LDS reads are outstanding.  LDS reads complete in
+// issue order, so the older ones are done -- valid only while no scalar
+// memory load is outstanding (those share the counter but complete out of
+// order); callers drain the counter with lds_wait() first.
+template <int N>
+__device__ __forceinline__ void lds_wait_n() { asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(N) : "memory"); }
 // Ties a value to the preceding lds_wait() so no use is scheduled above it.
 __device__ __forceinline__ void lds_ready(u32x2& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void lds_ready(u32x4& x) { asm volatile("" : "+v"(x)); }
 
 template <typename F, int... I>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {

@@ -59,7 +59,10 @@ struct MergeParams {
 // Per-device one-time raise of a kernel's dynamic-LDS limit.
 hipError_t ensure_lds_limit(const void* fn, int bytes, std::atomic<unsigned>& done_mask);
 
-int prefill_bf16_block_k(int d);
+// Whether d uses the wide bf16 kernel (64 query rows per wave), and the query
+// rows of one bf16 workgroup tile for head dim d and qh heads per workgroup.
+bool prefill_bf16_wide(int d);
+int prefill_bf16_query_rows(int d, int qh);
 hipError_t launch_prefill_bf16(const PrefillParams& p, int d, int qh, int grid, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillParams& p, int d, int grid, hipStream_t stream);
 constexpr int kF32QueryTile = 128;   // query rows per fp32 workgroup
