@@ -59,9 +59,8 @@ struct MergeParams {
 // Per-device one-time raise of a kernel's dynamic-LDS limit.
 hipError_t ensure_lds_limit(const void* fn, int bytes, std::atomic<unsigned>& done_mask);
 
-// Whether d uses the wide bf16 kernel (64 query rows per wave), and the query
-// rows of one bf16 workgroup tile for head dim d and qh heads per workgroup.
-bool prefill_bf16_wide(int d);
+// Query rows of one bf16 workgroup tile for head dim d and qh query heads
+// per workgroup.
 int prefill_bf16_query_rows(int d, int qh);
 hipError_t launch_prefill_bf16(const PrefillParams& p, int d, int qh, int grid, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillParams& p, int d, int grid, hipStream_t stream);

@@ -30,21 +30,9 @@
 
 namespace fakv {
 
-#ifndef FAKV_ASM_LDS
-#define FAKV_ASM_LDS 1
-#endif
-#ifndef FAKV_WIDE
-#define FAKV_WIDE 0
-#endif
-#ifndef FAKV_WIDE_BK
-#define FAKV_WIDE_BK 32
-#endif
-
 // Lazy softmax shift: the running shift moves only when the row max exceeds
 // it by more than this many powers of two.
 constexpr float kLazyShift = 8.f;
-// The wide kernel's shift bound (powers of two), see prefill_item_wide.
-constexpr float kWideShift = 64.f;
 
 // Keys per tile by head dim: every K or V tile is 1024 16-byte slots (16 KB).
 template <int D> struct TileK { static constexpr int BK = 8192 / D; };
@@ -212,7 +200,6 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
     if (nxt.valid) issue_tile(nxt.kt, BUF ^ 1);
 
     const bool skip = !wave_active || (p.causal && p.prune && kt > qw_hi - 1 + delta);
-#if FAKV_ASM_LDS
     if constexpr (D <= 128) {
     if (!skip) {
       // Every LDS read below is inline asm with explicit lgkmcnt waits: the
@@ -322,9 +309,7 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
         });
       });
     }
-    } else
-#endif
-    {
+    } else {
     if (!skip) {
       const char* kl = smem + BUF * 2 * TILE;
       const char* vl = kl + TILE;
@@ -445,446 +430,11 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
   }
 }
 
-// ---------------------------------------------------------------------------
-// Wide variant for d = 64 / 128: 64 query rows per wave (two 32-column MFMA
-// blocks), one wave per SIMD.  Every K or V operand read from LDS feeds two
-// MFMAs, halving LDS read traffic per FLOP -- with 32 rows per wave the LDS
-// reads, not the matrix cores, bound the kernel.  The wave runs a software
-// pipeline across tiles: the MFMAs of S(t+1) = K(t+1) Q^T are issued next to
-// the exponentials of tile t, then O += V(t) P(t).  Tiles rotate through four
-// LDS buffers (tile j in buffer j mod 4) and are prefetched three ahead, so
-// HBM latency hides behind two tiles of compute.
-
-template <int D> struct Wide {
-  static constexpr int BK = FAKV_WIDE_BK;       // keys per tile
-  static constexpr int TILE = BK * D * 2;       // bytes of one K or V tile
-  static constexpr int NBUF = 4;
-  static constexpr int LDS = NBUF * 2 * TILE;
-  static constexpr bool SPLIT = LDS > 65536;    // buffers 2-3 addressed from a second base
-};
-
-// Offset of buffer BUF from its base register.  With more than 64 KB of
-// buffers, buffers 0-1 are addressed from lb0 and 2-3 from lb1 = lb0 + 64 KB,
-// so every offset fits the 16-bit immediate of the DS instructions.
-template <int D, int BUF>
-struct WideBuf {
-  static constexpr int base = Wide<D>::SPLIT ? (BUF & 1) * 2 * Wide<D>::TILE : BUF * 2 * Wide<D>::TILE;
-  static constexpr bool hi = Wide<D>::SPLIT && BUF >= 2;
-};
-
-struct TileRef {
-  int kt, end, valid;
-};
-
 template <int D, int QH>
-__device__ __forceinline__ void prefill_item_wide(const PrefillParams& p, char* smem, const ItemGeo& g) {
-  constexpr int BK = Wide<D>::BK;
-  constexpr int WPH = 4 / QH;          // waves per query head
-  constexpr int KB = BK / 32;          // 32-key MFMA blocks per tile
-  constexpr int DS = D / 16;           // k-steps of S^T = K Q^T
-  constexpr int DB = D / 32;           // 32-dim blocks of O^T
-  constexpr int KS = BK / 16;          // k-steps of O^T += V^T P^T
-  constexpr int TILE = Wide<D>::TILE;
-  constexpr int NCH = D / 8;           // 16-byte chunks per key row
-  constexpr int NI = TILE / 16 / 256;  // DMA instructions per thread per tensor
-  static_assert(KB * 32 == BK && KS * 16 == BK && NI >= 1 && NI * 256 * 16 == TILE, "tile geometry");
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hl = wave / WPH;
-  const int qsub = wave % WPH;
-  const int half = lane >> 5;
-  const int col = lane & 31;
-
-  const int seq_q0 = g.seq_q0, seq_k0 = g.seq_k0, Lq = g.Lq, Lk = g.Lk;
-  const int q_lo = g.q_lo, q_hi = g.q_hi;
-  const int head = g.hg * QH + hl;
-  const int kvh = head / (p.h_q / p.h_kv);
-  const int delta = p.q_pos0 - p.k_pos0;
-  const int w = g.jagged ? (Lk + p.C - 1) / p.C : Lk / p.C;
-
-  KvWalk walk;
-  walk.S = Lk; walk.C = p.C; walk.w = w;
-  walk.r = (Lq > 0) ? (int)(((long long)q_lo * p.C) / Lq) : 0;
-  walk.q_hi = q_hi; walk.delta = delta; walk.causal = p.causal; walk.prune = p.prune;
-  walk.BK = BK;
-  walk.first();
-
-  // ---- this wave's 64 query rows: column block c holds rows qw_lo + 32 c + col
-  const int qw_lo = q_lo + 64 * qsub;
-  const int qw_hi = min(qw_lo + 64, q_hi);
-  const bool wave_active = qw_lo < q_hi;
-  int qi[2];
-  bool qvalid[2];
-  size_t qrow[2];
-  bf16x8 qreg[2][DS];
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    qi[c] = qw_lo + 32 * c + col;
-    qvalid[c] = qi[c] < q_hi;
-    qrow[c] = (size_t)(seq_q0 + qi[c]) * p.h_q + head;
-    const uint16_t* qp = p.q + qrow[c] * D + 8 * half;
-#pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (qvalid[c]) x = *reinterpret_cast<const u32x4*>(qp + 16 * s);
-      qreg[c][s] = __builtin_bit_cast(bf16x8, x);
-    }
-  }
-
-  // Running state per column block, as in the narrow kernel: l and O are kept
-  // relative to the lazily moved shift m_sh <= m_true.
-  f32x16 oacc[2][DB];
-  float m_true[2], m_sh[2], l_run[2];
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-#pragma unroll
-    for (int b = 0; b < DB; ++b) oacc[c][b] = f32x16{};
-    m_true[c] = m_sh[c] = neg_inf();
-    l_run[c] = 0.f;
-    if (p.mode == 2 && qvalid[c]) {
-      m_true[c] = m_sh[c] = p.m_st[qrow[c]];
-      l_run[c] = half == 0 ? p.l_st[qrow[c]] : 0.f;
-      const float* os = p.o_st + qrow[c] * D + 4 * half;
-#pragma unroll
-      for (int b = 0; b < DB; ++b)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          f32x4 x = *reinterpret_cast<const f32x4*>(os + 32 * b + 8 * gq);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) oacc[c][b][4 * gq + i] = x[i];
-        }
-    }
-  }
-
-  // ---- direct HBM -> LDS tile loads (same slot layout and swizzles as the
-  // narrow kernel; buffer resources bound every access to this sequence's rows)
-  const unsigned stride_b = (unsigned)p.h_kv * D * 2;
-  const size_t head_off = ((size_t)seq_k0 * p.h_kv + kvh) * D;
-  const unsigned extent = Lk > 0 ? (unsigned)(Lk - 1) * stride_b + D * 2 : 0u;
-  const __amdgpu_buffer_rsrc_t rs_k = make_rsrc(p.k + head_off, extent);
-  const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(p.v + head_off, extent);
-  unsigned voff_k[NI], voff_v[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int sl = (4 * i + wave) * 64 + lane;
-    const int r = sl / NCH, pc = sl % NCH;
-    voff_k[i] = (unsigned)r * stride_b + (unsigned)((pc ^ kmask<D>(r)) * 16);
-    voff_v[i] = (unsigned)r * stride_b + (unsigned)((pc ^ vmask<D>(r)) * 16);
-  }
-  auto buf_base = [&](int buf) -> char* {
-    return Wide<D>::SPLIT ? smem + (buf & 1) * 2 * TILE + (buf >> 1) * 65536 : smem + buf * 2 * TILE;
-  };
-  auto issue = [&](int kt, int buf) {
-    char* kl = buf_base(buf);
-    char* vl = kl + TILE;
-    const unsigned t0 = (unsigned)kt * stride_b;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int blk = 4 * i + wave;
-      dma16(rs_k, t0 + voff_k[i], kl + blk * 1024);
-      dma16(rs_v, t0 + voff_v[i], vl + blk * 1024);
-    }
-  };
-
-  int koff[DS];
-#pragma unroll
-  for (int s = 0; s < DS; ++s) koff[s] = col * (D * 2) + (((2 * s + half) ^ kmask<D>(col)) * 16);
-  int voff[DB];
-  {
-    const int vg16 = (lane >> 4) & 1, vp = lane & 15;
-    const int vrow = 4 * half + (vp >> 2);
-    const int vmsk = vmask<D>(vrow);
-#pragma unroll
-    for (int b = 0; b < DB; ++b)
-      voff[b] = vrow * (D * 2) + ((4 * b + 2 * vg16 + ((vp & 3) >> 1)) ^ vmsk) * 16 + (vp & 1) * 8;
-  }
-  const lds_char* lb0 = (const lds_char*)smem;
-  const lds_char* lb1 = lb0 + (Wide<D>::SPLIT ? 65536 : 0);
-
-  const float scale = p.scale;
-  const float scale_log2 = p.scale_log2;
-
-  auto wave_on = [&](int kt) -> bool {
-    return wave_active && !(p.causal && p.prune && kt > qw_hi - 1 + delta);
-  };
-
-  // S^T(tile in buffer BUF) = K Q^T for both column blocks; every K operand
-  // read serves two MFMAs.  K reads run one k-step ahead of the MFMAs.
-  auto qk = [&](auto bufc, f32x16 (&S)[2][KB]) {
-    constexpr int BUF = decltype(bufc)::value;
-    constexpr int KOFF = WideBuf<D, BUF>::base;
-    const lds_char* lb = WideBuf<D, BUF>::hi ? lb1 : lb0;
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int b = 0; b < KB; ++b) S[c][b] = f32x16{};
-    u32x4 ka[2][KB];
-    static_for<KB>([&](auto bc) {
-      constexpr int b = decltype(bc)::value;
-      ka[0][b] = ds_read16_at<KOFF + b * 32 * (D * 2)>(lb + koff[0]);
-    });
-    static_for<DS>([&](auto sc) {
-      constexpr int s = decltype(sc)::value;
-      if constexpr (s + 1 < DS) {
-        static_for<KB>([&](auto bc) {
-          constexpr int b = decltype(bc)::value;
-          ka[(s + 1) & 1][b] = ds_read16_at<KOFF + b * 32 * (D * 2)>(lb + koff[s + 1]);
-        });
-        lds_wait_n<KB>();
-      } else {
-        lds_wait_n<0>();
-      }
-      static_for<KB>([&](auto bc) {
-        constexpr int b = decltype(bc)::value;
-        lds_ready(ka[s & 1][b]);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, ka[s & 1][b]);
-        S[0][b] = mfma32x32x16(a, qreg[0][s], S[0][b]);
-        S[1][b] = mfma32x32x16(a, qreg[1][s], S[1][b]);
-      });
-    });
-  };
-
-  __shared__ int s_bail;     // set when some wave needs the fallback
-  bool bail = false;
-  // Online-softmax fold of one tile, part 1: element mask (only on tiles
-  // that cross the diagonal or the chunk's tail), row max, and the lazy shift
-  // move with its O rescale.  Returns the exp2 offsets in mlog.
-  auto fold_max = [&](f32x16 (&S)[2][KB], int kt, int end, float (&mlog)[2]) {
-    const bool need_mask = (kt + BK > end) || (p.causal && (kt + BK - 1 > qw_lo + delta));
-    if (need_mask) {
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int qlim = qi[c] + delta;
-#pragma unroll
-        for (int b = 0; b < KB; ++b)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kt + 32 * b + 8 * (r >> 2) + 4 * half + (r & 3);
-            const bool ok = key < end && (!p.causal || key <= qlim);
-            if (!ok) S[c][b][r] = neg_inf();
-          }
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      float mt = neg_inf();
-#pragma unroll
-      for (int b = 0; b < KB; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, S[c][b][r]);
-      mt = halves_max(mt);
-      m_true[c] = fmaxf(m_true[c], mt * scale);
-    }
-    // The shift is set once, from the first finite row max (O and l are
-    // still zero then, so nothing is rescaled), and then left alone unless
-    // the row max outgrows it by more than kWideShift powers of two: scaled
-    // exp terms stay <= 2^kWideShift, far inside fp32 and bf16 range.  Moving
-    // it later would mean rescaling O, which lives in accumulation registers
-    // the vector ALU cannot touch without copies that would crowd the loop;
-    // that (pathological) case is handed to the narrow kernel's algorithm.
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const bool fresh = m_sh[c] == neg_inf();
-      if (__builtin_amdgcn_ballot_w64(!fresh && m_true[c] > m_sh[c] + kWideShift * kLn2) != 0) bail = true;
-      m_sh[c] = fresh ? m_true[c] : m_sh[c];
-      mlog[c] = ((m_sh[c] == neg_inf()) ? 0.f : m_sh[c]) * kLog2e;
-    }
-  };
-  // Part 2: exponentials, row sums, P in bf16.  Straight-line code, so the
-  // scheduler can interleave it with the next tile's QK MFMAs.
-  auto fold_exp = [&](f32x16 (&S)[2][KB], const float (&mlog)[2], bf16x8 (&pb)[2][KS]) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-#pragma unroll
-      for (int b = 0; b < KB; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(__builtin_fmaf(S[c][b][r], scale_log2, -mlog[c]));
-          S[c][b][r] = e;
-          l_run[c] += e;
-        }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        float pv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pv[j] = S[c][ks >> 1][8 * (ks & 1) + j];
-        pb[c][ks] = pack_bf16x8(pv);
-      }
-    }
-  };
-
-  // O^T += V^T P^T from buffer BUF; every V operand read serves two MFMAs.
-  auto pv = [&](auto bufc, const bf16x8 (&pb)[2][KS]) {
-    constexpr int BUF = decltype(bufc)::value;
-    constexpr int VOFF = WideBuf<D, BUF>::base + TILE;
-    const lds_char* lb = WideBuf<D, BUF>::hi ? lb1 : lb0;
-    u32x2 va[2][DB][2];
-    auto issue_v = [&](auto ksc, auto slotc) {
-      constexpr int ks = decltype(ksc)::value;
-      constexpr int sl = decltype(slotc)::value;
-      static_for<DB>([&](auto bc) {
-        constexpr int b = decltype(bc)::value;
-        va[sl][b][0] = tr16_at<VOFF + 16 * ks * (D * 2)>(lb + voff[b]);
-        va[sl][b][1] = tr16_at<VOFF + 16 * ks * (D * 2) + 8 * (D * 2)>(lb + voff[b]);
-      });
-    };
-    issue_v(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-    static_for<KS>([&](auto ksc) {
-      constexpr int ks = decltype(ksc)::value;
-      if constexpr (ks + 1 < KS) {
-        issue_v(std::integral_constant<int, ks + 1>{}, std::integral_constant<int, (ks + 1) & 1>{});
-        lds_wait_n<2 * DB>();
-      } else {
-        lds_wait_n<0>();
-      }
-      static_for<DB>([&](auto bc) {
-        constexpr int b = decltype(bc)::value;
-        lds_ready(va[ks & 1][b][0]);
-        lds_ready(va[ks & 1][b][1]);
-        const u32x4 a4 = {va[ks & 1][b][0][0], va[ks & 1][b][0][1], va[ks & 1][b][1][0], va[ks & 1][b][1][1]};
-        const bf16x8 a = __builtin_bit_cast(bf16x8, a4);
-        oacc[0][b] = mfma32x32x16(a, pb[0][ks], oacc[0][b]);
-        oacc[1][b] = mfma32x32x16(a, pb[1][ks], oacc[1][b]);
-      });
-    });
-  };
-
-  // ---- the pipelined walk -------------------------------------------------
-  // Tiles t (scores in Sc), t+1 (its K is read this step), t+2 (landed or
-  // landing) and the walker at t+3 (prefetched this step).
-  TileRef t0{0, 0, 0}, t1{0, 0, 0}, t2{0, 0, 0};
-  auto take = [&](TileRef& r) {
-    r.kt = walk.kt; r.end = walk.end; r.valid = walk.valid;
-    if (walk.valid) walk.next();
-  };
-  take(t0);
-  take(t1);
-  take(t2);
-  if (tid == 0) s_bail = 0;
-  if (t0.valid) issue(t0.kt, 0);
-  if (t1.valid) issue(t1.kt, 1);
-  if (t2.valid) issue(t2.kt, 2);
-  // tiles 0 and 1 must be resident; tile 2 may still be in flight
-  if (t2.valid) vm_wait<2 * NI>(); else vm_wait<0>();
-  __syncthreads();
-
-  f32x16 Sa[2][KB], Sb[2][KB];
-  bool cur_on = t0.valid && wave_on(t0.kt);
-  lds_wait();                     // drain scalar loads: the LDS wait counts below are exact
-  if (cur_on) qk(std::integral_constant<int, 0>{}, Sa);
-
-  // One step on tile t in buffer BUF: prefetch tile t+3, S(t+1) = QK, fold
-  // tile t, O += PV(t), then wait for tile t+2 and synchronise.
-  auto step = [&](auto bufc, f32x16 (&Sc)[2][KB], f32x16 (&Sn)[2][KB]) {
-    constexpr int BUF = decltype(bufc)::value;
-    const bool pf = walk.valid;
-    if (pf) issue(walk.kt, (BUF + 3) & 3);
-    const bool next_on = t1.valid && wave_on(t1.kt);
-    lds_wait();
-    if (cur_on) {
-      float mlog[2];
-      fold_max(Sc, t0.kt, t0.end, mlog);
-      bf16x8 pb[2][KS];
-      if (next_on) {
-        qk(std::integral_constant<int, (BUF + 1) & 3>{}, Sn);
-        fold_exp(Sc, mlog, pb);
-      } else {
-        fold_exp(Sc, mlog, pb);
-      }
-      pv(std::integral_constant<int, BUF>{}, pb);
-    } else if (next_on) {
-      qk(std::integral_constant<int, (BUF + 1) & 3>{}, Sn);
-    }
-    if (bail && lane == 0) s_bail = 1;
-    if (pf) vm_wait<2 * NI>(); else vm_wait<0>();
-    __syncthreads();
-    cur_on = next_on;
-    t0 = t1;
-    t1 = t2;
-    take(t2);
-  };
-  bool bailed = false;
-  while (t0.valid) {
-    step(std::integral_constant<int, 0>{}, Sa, Sb);
-    if ((bailed = s_bail != 0) || !t0.valid) break;
-    step(std::integral_constant<int, 1>{}, Sb, Sa);
-    if ((bailed = s_bail != 0) || !t0.valid) break;
-    step(std::integral_constant<int, 2>{}, Sa, Sb);
-    if ((bailed = s_bail != 0) || !t0.valid) break;
-    step(std::integral_constant<int, 3>{}, Sb, Sa);
-    if ((bailed = s_bail != 0)) break;
-  }
-  if (bailed) {
-    // Recompute the tile with the narrow algorithm, which moves the shift
-    // whenever needed: its two halves of 32 rows per wave.  Nothing has been
-    // written yet; drain the prefetches before the LDS is reused.
-    vm_wait<0>();
-    __syncthreads();
-    constexpr int HALF = 32 * WPH;
-    ItemGeo h = g;
-    h.q_hi = min(g.q_lo + HALF, g.q_hi);
-    prefill_item<D, QH>(p, smem, h);
-    __syncthreads();
-    if (g.q_lo + HALF < g.q_hi) {
-      h.q_lo = g.q_lo + HALF;
-      h.q_hi = g.q_hi;
-      prefill_item<D, QH>(p, smem, h);
-      __syncthreads();
-    }
-    return;
-  }
-
-  // ---- epilogue -------------------------------------------------------------
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    float l_tot = halves_sum(l_run[c]);
-    if (!qvalid[c]) continue;
-    if (p.mode == 0) {
-      const float inv = 1.f / l_tot;
-      uint16_t* op = p.o + qrow[c] * D + 4 * half;
-#pragma unroll
-      for (int b = 0; b < DB; ++b)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          u32x2 x = {pack_bf16x2(oacc[c][b][4 * gq] * inv, oacc[c][b][4 * gq + 1] * inv),
-                     pack_bf16x2(oacc[c][b][4 * gq + 2] * inv, oacc[c][b][4 * gq + 3] * inv)};
-          *reinterpret_cast<u32x2*>(op + 32 * b + 8 * gq) = x;
-        }
-    } else {
-      const float f = (m_true[c] == neg_inf()) ? 1.f : fast_exp2((m_sh[c] - m_true[c]) * kLog2e);
-      l_tot *= f;
-      if (half == 0) {
-        p.m_st[qrow[c]] = m_true[c];
-        p.l_st[qrow[c]] = l_tot;
-      }
-      float* os = p.o_st + qrow[c] * D + 4 * half;
-#pragma unroll
-      for (int b = 0; b < DB; ++b)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          f32x4 x = {oacc[c][b][4 * gq] * f, oacc[c][b][4 * gq + 1] * f, oacc[c][b][4 * gq + 2] * f,
-                     oacc[c][b][4 * gq + 3] * f};
-          *reinterpret_cast<f32x4*>(os + 32 * b + 8 * gq) = x;
-        }
-    }
-  }
-}
-
-template <int D, int QH, int WIDE>
-__device__ __forceinline__ void run_item(const PrefillParams& p, char* smem, const ItemGeo& g) {
-  if constexpr (WIDE) prefill_item_wide<D, QH>(p, smem, g);
-  else prefill_item<D, QH>(p, smem, g);
-}
-
-template <int D, int QH, int WIDE>
-__global__ __launch_bounds__(256, WIDE ? 1 : 2)
+__global__ __launch_bounds__(256, 2)
 void prefill_bf16_kernel(PrefillParams p) {
-  constexpr int BQ = (WIDE ? 64 : 32) * (4 / QH);
-  // narrow: K0 V0 K1 V1 of 16 KB; wide: four K/V buffer pairs
-  // (the wide kernel's fallback runs the narrow algorithm in the same LDS)
-  __shared__ __attribute__((aligned(16))) char smem[(WIDE && Wide<D>::LDS > 4 * 16384) ? Wide<D>::LDS : 4 * 16384];
+  constexpr int BQ = 32 * (4 / QH);
+  __shared__ __attribute__((aligned(16))) char smem[4 * 16384];  // K0 V0 K1 V1
 
   if (p.sched != nullptr) {
     // Jagged batch, persistent: pop entries (item * n_hg + head group) from
@@ -920,7 +470,7 @@ void prefill_bf16_kernel(PrefillParams p) {
       g.q_hi = it[6] - it[2];
       g.hg = e - item * p.n_hg;
       g.jagged = 1;
-      run_item<D, QH, WIDE>(p, smem, g);
+      prefill_item<D, QH>(p, smem, g);
     }
     return;
   }
@@ -957,45 +507,43 @@ void prefill_bf16_kernel(PrefillParams p) {
   g.q_lo = qt * BQ;
   g.q_hi = min(g.q_lo + BQ, g.Lq);
   g.jagged = 0;
-  run_item<D, QH, WIDE>(p, smem, g);
+  prefill_item<D, QH>(p, smem, g);
 }
 
-// The wide kernel serves d = 64 and 128; d = 256 keeps 32 rows per wave (its
-// accumulators alone fill the register budget of 64 rows).
-bool prefill_bf16_wide(int d) { return FAKV_WIDE && d <= 128; }
+int prefill_bf16_query_rows(int d, int qh) {
+  (void)d;
+  return 32 * (4 / qh);
+}
 
-int prefill_bf16_query_rows(int d, int qh) { return (prefill_bf16_wide(d) ? 64 : 32) * (4 / qh); }
-
-template <int D, int QH, int WIDE>
+template <int D, int QH>
 static hipError_t launch_one(const PrefillParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, QH, WIDE>), dim3(grid), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, QH>), dim3(grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, int WIDE>
+template <int D>
 static hipError_t launch_qh(const PrefillParams& p, int qh, int grid, hipStream_t stream) {
   switch (qh) {
-    case 1: return launch_one<D, 1, WIDE>(p, grid, stream);
-    case 2: return launch_one<D, 2, WIDE>(p, grid, stream);
-    case 4: return launch_one<D, 4, WIDE>(p, grid, stream);
+    case 1: return launch_one<D, 1>(p, grid, stream);
+    case 2: return launch_one<D, 2>(p, grid, stream);
+    case 4: return launch_one<D, 4>(p, grid, stream);
   }
   return hipErrorInvalidValue;
 }
 
-template <int D, int QH, int WIDE>
+template <int D, int QH>
 static int resident_per_cu() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_bf16_kernel<D, QH, WIDE>, 256, 0) != hipSuccess) n = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_bf16_kernel<D, QH>, 256, 0) != hipSuccess) n = 1;
   return n > 0 ? n : 1;
 }
 
 template <int D>
 static int resident_qh(int qh) {
-  constexpr int W = (FAKV_WIDE && D <= 128) ? 1 : 0;
   switch (qh) {
-    case 1: return resident_per_cu<D, 1, W>();
-    case 2: return resident_per_cu<D, 2, W>();
-    default: return resident_per_cu<D, 4, W>();
+    case 1: return resident_per_cu<D, 1>();
+    case 2: return resident_per_cu<D, 2>();
+    default: return resident_per_cu<D, 4>();
   }
 }
 
@@ -1016,9 +564,9 @@ int prefill_bf16_persistent_grid(int d, int qh) {
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, int d, int qh, int grid, hipStream_t stream) {
   switch (d) {
-    case 64: return launch_qh<64, FAKV_WIDE>(p, qh, grid, stream);
-    case 128: return launch_qh<128, FAKV_WIDE>(p, qh, grid, stream);
-    case 256: return launch_qh<256, 0>(p, qh, grid, stream);
+    case 64: return launch_qh<64>(p, qh, grid, stream);
+    case 128: return launch_qh<128>(p, qh, grid, stream);
+    case 256: return launch_qh<256>(p, qh, grid, stream);
   }
   return hipErrorInvalidValue;
 }
