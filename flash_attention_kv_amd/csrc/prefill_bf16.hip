@@ -437,40 +437,47 @@ void prefill_bf16_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) char smem[4 * 16384];  // K0 V0 K1 V1
 
   if (p.sched != nullptr) {
-    // Jagged batch, persistent: pop entries (item * n_hg + head group) from
-    // this XCD's queue -- workgroup L runs on XCD L % 8 -- then steal from
-    // the other queues.  Each queue holds whole (sequence, head group) units,
-    // longest first, so the query tiles that share one sequence's K/V run
-    // together on one XCD and hit its L2.  Every workgroup exits once all
-    // eight queues are drained.
-    __shared__ int s_entry;
-    const int x0 = blockIdx.x & 7;
-    for (;;) {
-      if (threadIdx.x == 0) {
-        int e = -1;
-        for (int q = 0; q < 8 && e < 0; ++q) {
-          const int x = (x0 + q) & 7;
-          const int len = p.qinfo[x];
-          if (__hip_atomic_load(&p.qinfo[8 + x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= len) continue;
-          const int slot = atomicAdd(&p.qinfo[8 + x], 1);
-          if (slot < len) e = p.sched[(size_t)x * p.sched_stride + slot];
-        }
-        s_entry = e;
-      }
-      __syncthreads();
-      const int e = s_entry;
-      __syncthreads();
-      if (e < 0) break;
+    // Jagged batch, persistent and statically scheduled.  Queue x holds the
+    // entries (item * n_hg + head group) meant for XCD x -- workgroup L runs
+    // on XCD L % 8 -- as whole (sequence, head group) units, longest first,
+    // so the query tiles that share one sequence's K/V run on one XCD and
+    // hit its L2.  The grid is a multiple of 8; the G / 8 workgroups of XCD x
+    // deal the entries of queue x among themselves in zigzag rounds.  No
+    // atomics: every workgroup knows its entries,
+    // so the next entry and its item record are fetched while the current
+    // item computes.
+    const int x = blockIdx.x & 7;
+    const int nj = gridDim.x >> 3;
+    const int len = p.qinfo[x];
+    const int* q = p.sched + (size_t)x * p.sched_stride;
+    auto load = [&](int slot, ItemGeo& g) -> bool {
+      if (slot >= len) return false;
+      const int e = q[slot];
       const int item = e / p.n_hg;
       const int32_t* it = p.items + 8 * (size_t)item;
-      ItemGeo g;
       g.seq_q0 = g.seq_k0 = it[2];
       g.Lq = g.Lk = it[3];
       g.q_lo = it[4] - it[2];
       g.q_hi = it[6] - it[2];
       g.hg = e - item * p.n_hg;
       g.jagged = 1;
+      return true;
+    };
+    // Round r covers slots [r nj, (r + 1) nj); workgroup j takes slot j of
+    // even rounds and slot nj - 1 - j of odd ones, so a workgroup that drew a
+    // long tile of a unit draws a short one next.
+    const int j = blockIdx.x >> 3;
+    auto slot_of = [&](int r) { return r * nj + ((r & 1) ? nj - 1 - j : j); };
+    int r = 0;
+    ItemGeo g;
+    bool have = load(slot_of(0), g);
+    while (have) {
+      ItemGeo gn;
+      const bool have_n = load(slot_of(r + 1), gn);
       prefill_item<D, QH>(p, smem, g);
+      ++r;
+      g = gn;
+      have = have_n;
     }
     return;
   }
@@ -557,7 +564,9 @@ int prefill_bf16_persistent_grid(int d, int qh) {
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
   const int per = d == 64 ? resident_qh<64>(qh) : d == 128 ? resident_qh<128>(qh) : resident_qh<256>(qh);
-  g = per * cus;
+  // a multiple of 8 (one share per XCD queue), at least 8
+  g = ((per * cus) / 8) * 8;
+  if (g < 8) g = 8;
   cache[dev & 31][key].store(g, std::memory_order_relaxed);
   return g;
 }

@@ -82,7 +82,7 @@ void worklist_kernel(const int32_t* __restrict__ off, int n_seqs, int total, int
 // (sequence, head group) pairs; sequences are ranked by tile count, longest
 // first, and the units of that order are dealt round-robin onto 8 queues
 // (unit k -> queue k mod 8).  A unit's entries -- its query tiles, longest
-// first -- are contiguous in its queue, so the workgroups that pop them run
+// first -- are contiguous in its queue, so the workgroups that take them run
 // at the same time on one XCD and share that sequence's K/V in its L2.
 // Entry = record index * n_hg + head group.  Runs after worklist_kernel on
 // the same stream; an empty worklist gives empty queues.
@@ -185,10 +185,7 @@ void schedule_kernel(const int32_t* __restrict__ off, int n_seqs, int BQ, const 
     if (tid >= 1016) s_carry[x] += s_val[tid];
     __syncthreads();
   }
-  if (tid < 8) {
-    sb.qinfo[tid] = s_carry[tid];
-    sb.qinfo[8 + tid] = 0;
-  }
+  if (tid < 8) sb.qinfo[tid] = s_carry[tid];
 }
 
 hipError_t launch_schedule(const int32_t* seq_offsets, int n_seqs, int BQ, const int32_t* items,
