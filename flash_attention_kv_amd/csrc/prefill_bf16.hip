@@ -172,16 +172,21 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
   // Lane-constant LDS read offsets (bytes within a tile).  The swizzles make
   // them non-linear in the k-step / dim block, so they are computed once here;
   // inside the loop every address is one of these plus an immediate.
-  int koff[DS];                                          // + 32 b rows
+  // The swizzle masks are < 16 chunks, so k-step s >= 8 (d = 256) is k-step
+  // s - 8 plus 256 bytes, and dim block b >= 4 is block b - 4 plus 256 bytes:
+  // KR / VR registers serve every step, the rest folds into immediates.
+  constexpr int KR = DS < 8 ? DS : 8;
+  constexpr int VR = DB < 4 ? DB : 4;
+  int koff[KR];                                          // + 32 b rows
 #pragma unroll
-  for (int s = 0; s < DS; ++s) koff[s] = col * (D * 2) + (((2 * s + half) ^ kmask<D>(col)) * 16);
-  int voff[DB];                                          // + 16 ks rows (+ 8 rows)
+  for (int s = 0; s < KR; ++s) koff[s] = col * (D * 2) + (((2 * s + half) ^ kmask<D>(col)) * 16);
+  int voff[VR];                                          // + 16 ks rows (+ 8 rows)
   {
     const int vg16 = (lane >> 4) & 1, vp = lane & 15;
     const int vrow = 4 * half + (vp >> 2);
     const int vmsk = vmask<D>(vrow);
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
+    for (int b = 0; b < VR; ++b)
       voff[b] = vrow * (D * 2) + ((4 * b + 2 * vg16 + ((vp & 3) >> 1)) ^ vmsk) * 16 + (vp & 1) * 8;
   }
 
@@ -200,6 +205,8 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
     if (nxt.valid) issue_tile(nxt.kt, BUF ^ 1);
 
     const bool skip = !wave_active || (p.causal && p.prune && kt > qw_hi - 1 + delta);
+    // (d = 256 keeps the builtin reads: the extra staging registers of the
+    // asm path push it into spills.)
     if constexpr (D <= 128) {
     if (!skip) {
       // Every LDS read below is inline asm with explicit lgkmcnt waits: the
@@ -224,7 +231,7 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
         if constexpr (s + 1 < DS) {
           static_for<KB>([&](auto bc) {
             constexpr int b = decltype(bc)::value;
-            ka[(s + 1) & 1][b] = ds_read16_at<KOFF + b * 32 * (D * 2)>(lb + koff[s + 1]);
+            ka[(s + 1) & 1][b] = ds_read16_at<KOFF + b * 32 * (D * 2) + ((s + 1) / 8) * 256>(lb + koff[(s + 1) % 8]);
           });
           lds_wait_n<KB>();
         } else {
@@ -236,15 +243,21 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
           sacc[b] = mfma32x32x16(__builtin_bit_cast(bf16x8, ka[s & 1][b]), qreg[s], sacc[b]);
         });
       });
-      // first k-step of V^T in flight while the softmax runs
-      u32x2 va[2][DB][2];
-      auto issue_v = [&](auto ksc, auto slotc) {
-        constexpr int ks = decltype(ksc)::value;
+      // V^T reads go in groups of VG dim blocks (2 VG reads, within the
+      // lgkmcnt range), one group ahead of the MFMAs; the first group is in
+      // flight while the softmax runs.
+      constexpr int VG = DB < 4 ? DB : 4;
+      constexpr int NG = DB / VG;
+      u32x2 va[2][VG][2];
+      auto issue_v = [&](auto ic, auto slotc) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int ks = i / NG, g0 = (i % NG) * VG;
         constexpr int sl = decltype(slotc)::value;
-        static_for<DB>([&](auto bc) {
+        static_for<VG>([&](auto bc) {
           constexpr int b = decltype(bc)::value;
-          va[sl][b][0] = tr16_at<VOFF + 16 * ks * (D * 2)>(lb + voff[b]);
-          va[sl][b][1] = tr16_at<VOFF + 16 * ks * (D * 2) + 8 * (D * 2)>(lb + voff[b]);
+          constexpr int VI = VOFF + 16 * ks * (D * 2) + ((g0 + b) / 4) * 256;
+          va[sl][b][0] = tr16_at<VI>(lb + voff[(g0 + b) % 4]);
+          va[sl][b][1] = tr16_at<VI + 8 * (D * 2)>(lb + voff[(g0 + b) % 4]);
         });
       };
       issue_v(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
@@ -287,25 +300,30 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
           sacc[b][r] = e;
           l_run += e;
         }
-      // O^T += V^T P^T, V reads one k-step ahead of the MFMAs
-      static_for<KS>([&](auto ksc) {
-        constexpr int ks = decltype(ksc)::value;
-        if constexpr (ks + 1 < KS) {
-          issue_v(std::integral_constant<int, ks + 1>{}, std::integral_constant<int, (ks + 1) & 1>{});
-          lds_wait_n<2 * DB>();
-        } else {
-          lds_wait_n<0>();
-        }
+      // O^T += V^T P^T
+      bf16x8 pb[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
         float pv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) pv[j] = sacc[ks >> 1][8 * (ks & 1) + j];
-        const bf16x8 pb = pack_bf16x8(pv);
-        static_for<DB>([&](auto bc) {
+        pb[ks] = pack_bf16x8(pv);
+      }
+      static_for<KS * NG>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int ks = i / NG, g0 = (i % NG) * VG;
+        if constexpr (i + 1 < KS * NG) {
+          issue_v(std::integral_constant<int, i + 1>{}, std::integral_constant<int, (i + 1) & 1>{});
+          lds_wait_n<2 * VG>();
+        } else {
+          lds_wait_n<0>();
+        }
+        static_for<VG>([&](auto bc) {
           constexpr int b = decltype(bc)::value;
-          lds_ready(va[ks & 1][b][0]);
-          lds_ready(va[ks & 1][b][1]);
-          const u32x4 a4 = {va[ks & 1][b][0][0], va[ks & 1][b][0][1], va[ks & 1][b][1][0], va[ks & 1][b][1][1]};
-          oacc[b] = mfma32x32x16(__builtin_bit_cast(bf16x8, a4), pb, oacc[b]);
+          lds_ready(va[i & 1][b][0]);
+          lds_ready(va[i & 1][b][1]);
+          const u32x4 a4 = {va[i & 1][b][0][0], va[i & 1][b][0][1], va[i & 1][b][1][0], va[i & 1][b][1][1]};
+          oacc[g0 + b] = mfma32x32x16(__builtin_bit_cast(bf16x8, a4), pb[ks], oacc[g0 + b]);
         });
       });
     }
@@ -321,7 +339,7 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
       for (int s = 0; s < DS; ++s) {
 #pragma unroll
         for (int b = 0; b < KB; ++b) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl + koff[s] + b * 32 * (D * 2));
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl + koff[s % 8] + (s / 8) * 256 + b * 32 * (D * 2));
           sacc[b] = mfma32x32x16(a, qreg[s], sacc[b]);
         }
       }
@@ -376,7 +394,7 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
         const bf16x8 pb = pack_bf16x8(pv);
 #pragma unroll
         for (int b = 0; b < DB; ++b) {
-          const char* a1 = vl + voff[b] + 16 * ks * (D * 2);
+          const char* a1 = vl + voff[b % 4] + (b / 4) * 256 + 16 * ks * (D * 2);
           const bf16x4 lo = tr16(a1);
           const bf16x4 hi = tr16(a1 + 8 * (D * 2));
           const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
