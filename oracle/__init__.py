@@ -30,13 +30,15 @@ Parity status: every function here is pinned by the CPU tests in
 cross-check, high-precision spot checks, hand-derived fixtures and the pages'
 invariants).  No function is "parity unpinned".
 """
-from .attention import attention_ref, attention_rows_ref, softmax_scale, kv_head_of
+from .attention import attention_ref, attention_rows_ref, softmax_scale, kv_head_of, admissible
 from .triplet import (Triplet, identity_triplet, partial_ref, merge_ref, finalize_ref,
-                      ring_order, ring_ref, dependent_trip, tiled_fold_ref, attn_partial_ref)
+                      ring_order, ring_ref, dependent_trip, dependent_range, tiled_fold_ref,
+                      attn_partial_ref)
 from .worklist import WorkItem, worklist_ref, worklist_array_ref
 from .decode import (decode_partials_ref, splitkv_decode_ref, tree_merge_ref, chain_merge_ref,
                      fanout_order, fanout_simulate)
-from .counts import causal_pairs, prefill_pairs, useful_flops_prefill, decode_bytes, decode_flops
+from .counts import (causal_pairs, windowed_pairs, prefill_pairs, useful_flops_prefill, decode_bytes,
+                     decode_flops)
 
 __all__ = [
     "attention_ref", "attention_rows_ref", "softmax_scale", "kv_head_of",

@@ -20,6 +20,11 @@ Readings of what the pages leave open:
 * Causal.  The Helion page bounds the KV loop by the query tile's end; the
   element-level rule used here is key j admissible for query i iff j <= i,
   with query and key indices local to the sequence (top-left alignment).
+* Sliding window.  The Helion page ("Scalar minimum") leaves dependent lower
+  bounds to a later sliding-window feature without defining it; the reading
+  here is the causal window of W keys ending at the query: key j admissible
+  for query i iff i - W < j <= i (W >= 1; W = 1 is the query's own key, and
+  W >= the sequence length is plain causal attention).
 """
 from __future__ import annotations
 
@@ -54,8 +59,24 @@ def _attend(qr: np.ndarray, kk: np.ndarray, vv: np.ndarray, allowed: np.ndarray,
     return (e @ vv) / den, M[:, 0] + np.log(den[:, 0])
 
 
+def admissible(ii: np.ndarray, jj: np.ndarray, causal: bool, window=None) -> np.ndarray:
+    """Boolean (len(ii), len(jj)): key jj admissible for query ii (sequence-
+    local indices) under the causal rule and, if given, the sliding window."""
+    if window is not None:
+        if not causal:
+            raise ValueError("a sliding window is defined for causal attention only")
+        if window < 1:
+            raise ValueError("window must be >= 1")
+    if not causal:
+        return np.ones((len(ii), len(jj)), bool)
+    ok = jj[None, :] <= ii[:, None]
+    if window is not None:
+        ok &= (ii[:, None] - jj[None, :]) < window
+    return ok
+
+
 def attention_ref(q, k, v, *, causal: bool = False, n_seqs: int = 1, seq_offsets=None,
-                  return_lse: bool = False, rows_per_block: int = 4096):
+                  return_lse: bool = False, rows_per_block: int = 4096, window=None):
     """O (tokens, h_q, d) float64 for Q (tokens, h_q, d), K/V (tokens, h_kv, d).
 
     Dense batch when ``seq_offsets`` is None (``n_seqs`` equal sequences),
@@ -76,7 +97,7 @@ def attention_ref(q, k, v, *, causal: bool = False, n_seqs: int = 1, seq_offsets
             for r0 in range(q0, q1, rows_per_block):
                 r1 = min(q1, r0 + rows_per_block)
                 ii = np.arange(r0 - q0, r1 - q0)
-                allowed = (jj[None, :] <= ii[:, None]) if causal else np.ones((r1 - r0, k1 - k0), bool)
+                allowed = admissible(ii, jj, causal, window)
                 o, l = _attend(q[r0:r1, h], kk, vv, allowed, scale)
                 out[r0:r1, h] = o
                 lse[r0:r1, h] = l
@@ -84,7 +105,7 @@ def attention_ref(q, k, v, *, causal: bool = False, n_seqs: int = 1, seq_offsets
 
 
 def attention_rows_ref(q, k, v, tokens, heads, *, causal: bool = False, n_seqs: int = 1,
-                       seq_offsets=None):
+                       seq_offsets=None, window=None):
     """Selected output rows O[tokens[n], heads[n], :] (float64, (n, d)), each
     evaluated from the definition on its own (for spot checks at full size)."""
     T, h_q, d = q.shape
@@ -102,6 +123,6 @@ def attention_rows_ref(q, k, v, tokens, heads, *, causal: bool = False, n_seqs: 
         qr = f64(q[t, h]).reshape(1, d)
         kk, vv = f64(k[k0:k1, kv]), f64(v[k0:k1, kv])
         jj = np.arange(k1 - k0)
-        allowed = (jj <= t - q0)[None, :] if causal else np.ones((1, k1 - k0), bool)
+        allowed = admissible(np.array([t - q0]), jj, causal, window)
         res[n] = _attend(qr, kk, vv, allowed, scale)[0][0]
     return res

@@ -18,7 +18,22 @@ def causal_pairs(L: int) -> int:
     return L * (L + 1) // 2
 
 
-def prefill_pairs(T_q: int, S_kv: int, *, causal: bool, n_seqs: int = 1, seq_offsets=None) -> int:
+def windowed_pairs(L: int, W: int) -> int:
+    """Admissible pairs of a causal sliding window of W keys over L tokens:
+    query i sees min(i + 1, W) keys."""
+    if W >= L:
+        return causal_pairs(L)
+    return causal_pairs(W) + (L - W) * W
+
+
+def prefill_pairs(T_q: int, S_kv: int, *, causal: bool, n_seqs: int = 1, seq_offsets=None,
+                  window=None) -> int:
+    if window is not None:
+        if not causal:
+            raise ValueError("a sliding window is defined for causal attention only")
+        Ls = (np.diff(np.asarray(seq_offsets, dtype=np.int64)) if seq_offsets is not None
+              else [T_q // n_seqs] * n_seqs)
+        return int(sum(windowed_pairs(int(L), window) for L in Ls))
     if seq_offsets is not None:
         Ls = np.diff(np.asarray(seq_offsets, dtype=np.int64))
         if causal:

@@ -32,7 +32,7 @@ from dataclasses import dataclass
 import numpy as np
 
 from ._util import f64, segments
-from .attention import softmax_scale, kv_head_of
+from .attention import softmax_scale, kv_head_of, admissible
 
 
 @dataclass
@@ -93,21 +93,42 @@ def dependent_trip(begin: int, kv_end: int, q_tile_end: int, block_k: int, causa
     return (max(0, -(-n // block_k)), active_end)
 
 
+def dependent_range(begin: int, kv_end: int, q_tile_begin: int, q_tile_end: int, block_k: int,
+                    causal: bool, prune: bool = True, window=None):
+    """(first_tile, trip_count, active_begin, active_end) of one KV range
+    [begin, kv_end) for the query tile [q_tile_begin, q_tile_end) on a tile
+    grid starting at ``begin``.  Causal and pruned: the loop ends at
+    min(kv_end, q_tile_end) (the Helion page's dependent end) and, with a
+    sliding window W, starts at the tile holding max(begin, q_tile_begin - W + 1)
+    -- the dependent lower bound the page defers.  Unpruned: the whole range."""
+    trip, active_end = dependent_trip(begin, kv_end, q_tile_end, block_k, causal, prune)
+    active_begin, first = begin, 0
+    if causal and prune and window is not None:
+        active_begin = max(begin, q_tile_begin - window + 1)
+        first = max(0, (active_begin - begin) // block_k)
+        trip = max(0, trip - first)
+    return first, trip, active_begin, active_end
+
+
 def tiled_fold_ref(state: Triplet, qr, q_pos, kk, vv, k_pos0: int, block_k: int, causal: bool,
-                   q_tile_end: int, scale: float, prune: bool = True) -> Triplet:
+                   q_tile_end: int, scale: float, prune: bool = True, window=None,
+                   q_tile_begin: int = 0) -> Triplet:
     """Fold one KV chunk (keys at positions k_pos0 .. k_pos0 + n - 1) into
     ``state`` tile by tile, the way the dependent-bound loop runs: tile t covers
     keys [k_pos0 + t*block_k, ... + block_k), keys at or past active_end are
     masked, and (causal) key position <= query position is required."""
     n = kk.shape[0]
-    trip, active_end = dependent_trip(k_pos0, k_pos0 + n, q_tile_end, block_k, causal, prune)
+    first, trip, _, active_end = dependent_range(k_pos0, k_pos0 + n, q_tile_begin, q_tile_end, block_k,
+                                                 causal, prune, window)
     q_pos = np.asarray(q_pos)
-    for t in range(trip):
+    for t in range(first, first + trip):
         idx = k_pos0 + t * block_k + np.arange(block_k)
         mask_k = idx < active_end
         allowed = np.broadcast_to(mask_k[None, :], (len(q_pos), block_k))
         if causal:
             allowed = allowed & (idx[None, :] <= q_pos[:, None])
+            if window is not None:
+                allowed = allowed & (q_pos[:, None] - idx[None, :] < window)
         loc = np.clip(idx - k_pos0, 0, n - 1)   # masked slots never contribute
         state = merge_ref(state, partial_ref(qr, kk[loc], vv[loc], allowed, scale))
     return state
@@ -124,12 +145,13 @@ def _chunks(L: int, C: int, jagged: bool):
 
 
 def ring_ref(q, k, v, C: int, *, causal: bool = False, n_seqs: int = 1, seq_offsets=None,
-             block_k=None, prune: bool = True, return_triplet: bool = False):
+             block_k=None, prune: bool = True, return_triplet: bool = False, window=None):
     """Ring-KV prefill as the GQA prefill page runs it, one sequence at a time:
     each rank starts from the identity, visits chunks in ring order, skips a
-    chunk whole when (causal) it starts at or after the rank's last query + 1,
+    chunk whole when (causal) it starts at or after the rank's last query + 1
+    (or, with a sliding window W, ends at or before its first query - W + 1),
     folds every other chunk (in one partial, or tile by tile with the
-    dependent bound when ``block_k`` is given), and finally divides by l."""
+    dependent bounds when ``block_k`` is given), and finally divides by l."""
     q, k, v = f64(q), f64(k), f64(v)
     T, h_q, d = q.shape
     S, h_kv, _ = k.shape
@@ -150,19 +172,20 @@ def ring_ref(q, k, v, C: int, *, causal: bool = False, n_seqs: int = 1, seq_offs
                     continue
                 qr = q[q0 + rows, h]
                 st = identity_triplet(rows.size, d)
-                last = int(rows.max())
+                last, first_row = int(rows.max()), int(rows.min())
                 for c in ring_order(r, C):
                     c0, c1 = chunks[c]
                     if c1 <= c0 or (causal and c0 >= last + 1):
                         continue
+                    if window is not None and prune and c1 <= first_row - window + 1:
+                        continue
                     kk, vv = k[k0 + c0:k0 + c1, kv], v[k0 + c0:k0 + c1, kv]
                     if block_k is None:
-                        jj = np.arange(c0, c1)
-                        allowed = (jj[None, :] <= rows[:, None]) if causal else np.ones((rows.size, c1 - c0), bool)
+                        allowed = admissible(rows, np.arange(c0, c1), causal, window)
                         st = merge_ref(st, partial_ref(qr, kk, vv, allowed, scale))
                     else:
                         st = tiled_fold_ref(st, qr, rows, kk, vv, c0, block_k, causal, last + 1,
-                                            scale, prune)
+                                            scale, prune, window, first_row)
                 out[q0 + rows, h] = finalize_ref(st)
                 m_all[q0 + rows, h], l_all[q0 + rows, h] = st.m, st.l
     return (out, m_all, l_all) if return_triplet else out

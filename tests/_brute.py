@@ -3,8 +3,9 @@ the oracle.  Independent of oracle/: different code, different arithmetic."""
 import math
 
 
-def brute_attention(q, k, v, causal):
-    """q: [T][h_q][d], k, v: [S][h_kv][d] nested lists.  Returns [T][h_q][d]."""
+def brute_attention(q, k, v, causal, window=None):
+    """q: [T][h_q][d], k, v: [S][h_kv][d] nested lists.  Returns [T][h_q][d].
+    window W (causal only): query i sees keys i - W < j <= i."""
     T, h_q, d = len(q), len(q[0]), len(q[0][0])
     S, h_kv = len(k), len(k[0])
     g = h_q // h_kv
@@ -14,7 +15,7 @@ def brute_attention(q, k, v, causal):
         row = []
         for h in range(h_q):
             kv = h // g
-            js = [j for j in range(S) if (not causal or j <= i)]
+            js = [j for j in range(S) if (not causal or j <= i) and (window is None or i - j < window)]
             sc = [scale * math.fsum(q[i][h][t] * k[j][kv][t] for t in range(d)) for j in js]
             mx = max(sc)
             w = [math.exp(s - mx) for s in sc]

@@ -83,3 +83,33 @@ def test_wrong_fanout_order_is_caught(monkeypatch):
 def test_half_square_pair_count_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "causal_pairs", lambda L: L * L // 2)
     _fails(WD.test_counts_closed_forms_and_brute_force)
+
+
+def test_window_off_by_one_is_caught(monkeypatch):
+    from tests import test_oracle_window as WIN
+
+    def bad_admissible(ii, jj, causal, window=None):
+        ok = jj[None, :] <= ii[:, None]
+        if window is not None:
+            ok &= (ii[:, None] - jj[None, :]) <= window      # one key too many
+        return ok
+    monkeypatch.setattr(oatt, "admissible", bad_admissible)
+    monkeypatch.setattr(otri, "admissible", bad_admissible)
+    _fails(WIN.test_window_one_returns_own_value)
+    _fails(WIN.test_window_brute_force, 5, 2, (1, 1))
+
+
+def test_window_lower_bound_too_late_is_caught(monkeypatch):
+    from tests import test_oracle_window as WIN
+    good = otri.dependent_range
+
+    def late(begin, kv_end, qb, qe, bk, causal, prune=True, window=None):
+        first, trip, ab, ae = good(begin, kv_end, qb, qe, bk, causal, prune, window)
+        if window is not None and causal and prune and trip > 1:
+            return first + 1, trip - 1, ab, ae                # skips an admissible tile
+        return first, trip, ab, ae
+    monkeypatch.setattr(otri, "dependent_range", late)
+    # a row left without keys is refused outright; others come out wrong
+    for C, W in ((1, 17), (4, 64), (3, 5)):
+        with pytest.raises((AssertionError, ValueError)):
+            WIN.test_window_ring_equals_monolithic(C, W)
