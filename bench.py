@@ -8,7 +8,8 @@ heads over 8 KV heads, d = 128, 8192 tokens split into 8 ring chunks, bf16,
 causal): its value is useful causal TFLOP/s (4 d h_q per admissible
 (query, key) pair).  The same run measures, as extra entries, the dense causal
 d = 256 workload, the jagged 1152-sequence workload, the split-KV decode
-workload (HBM GB/s) and the 4-chunk fp32 ring latency case.
+workload (HBM GB/s), the GQA ring shape with a 2048-key causal sliding window
+and the 4-chunk fp32 ring latency case.
 
 Timing: W untimed warm-up steps, then K steps, each bracketed by HIP events
 recorded on the stream the library launches on (torch's current stream); the
@@ -97,12 +98,16 @@ def bench_prefill(name, steps, warmup, keep=False):
 
     def step():
         F.ring_attn_fwd(q, k, v, C=w.C, causal=w.causal, seq_offsets=offs_t, n_seqs=w.n_seqs,
-                        workspace=ws, out=o)
+                        workspace=ws, out=o, window=w.window)
 
     ms, wall = time_steps(step, steps, warmup, stream)
     if offs is not None:
         L = np.diff(offs.astype(np.int64))
         pairs = int((L * (L + 1) // 2).sum()) if w.causal else int((L * L).sum())
+    elif w.window is not None:
+        # query i sees min(i + 1, W) keys
+        L, W = w.T_q, w.window
+        pairs = w.n_seqs * (W * (W + 1) // 2 + max(0, L - W) * W if W < L else L * (L + 1) // 2)
     else:
         pairs = w.n_seqs * (w.T_q * (w.T_q + 1) // 2 if w.causal else w.T_q * w.S_kv)
     flops = 4 * w.d * w.h_q * pairs
@@ -177,7 +182,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workloads", default="gqa_ring,dense_causal,jagged,decode,ring_tiny")
+    ap.add_argument("--workloads", default="gqa_ring,dense_causal,jagged,gqa_swa,decode,ring_tiny")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run one device-to-device copy of BYTES (the reference kernel for "
@@ -207,7 +212,7 @@ def main():
     if "gqa_ring" in sel:
         head = bench_prefill("gqa_ring", args.steps, args.warmup, keep=not args.no_cpu_baseline)
         print(f"# gqa_ring: {head['ms']:.3f} ms/step, {head['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
-    for name in ("dense_causal", "jagged"):
+    for name in ("dense_causal", "jagged", "gqa_swa"):
         if name in sel:
             r = bench_prefill(name, args.steps, args.warmup)
             print(f"# {name}: {r['ms']:.3f} ms/step, {r['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
@@ -218,6 +223,8 @@ def main():
                                         "traffic": load_traffic(name)}}
     if "dense_causal" in extra:
         extra["dense_causal"]["page_context"] = "Pallas dense causal flash on the Helion page, same shape, unnamed chip: 225.8 TF/s"
+    if "gqa_swa" in extra:
+        extra["gqa_swa"]["window"] = 2048
     if "jagged" in extra:
         extra["jagged"]["page_context"] = "Helion page jagged table (softmax 'flash' row, unnamed chip, unknown lengths): 97.7 TF/s"
     if "decode" in sel:

@@ -26,6 +26,7 @@ SIGNATURES = {
     "attn_partial": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P]),
     "lse_merge": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _I, _P]),
     "ring_attn_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _I, _I, _P, _SZ, _P]),
+    "ring_attn_fwd_window": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _I, _I, _P, _SZ, _P]),
     "ring_attn_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I, _I, _I]),
     "splitkv_decode": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _SZ, _P]),
     "splitkv_decode_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
@@ -109,9 +110,11 @@ def splitkv_decode_workspace_bytes(B, h_q, d, n_chunks) -> int:
 def ring_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, C: int = 1,
                   causal: bool = False, seq_offsets: Optional[torch.Tensor] = None,
                   n_seqs: int = 1, workspace: Optional[torch.Tensor] = None,
-                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                  out: Optional[torch.Tensor] = None, window: Optional[int] = None) -> torch.Tensor:
     """Prefill attention.  q (n_seqs*T_q, h_q, d), k/v (n_seqs*S_kv, h_kv, d);
-    jagged when ``seq_offsets`` (int32, n_seqs+1, on the device) is given."""
+    jagged when ``seq_offsets`` (int32, n_seqs+1, on the device) is given.
+    ``window`` W (causal only): query i sees keys i - W < j <= i
+    (``ring_attn_fwd_window``)."""
     dev = _dev(q, k, v)
     dt = _dtype_code(q)
     if k.dtype != q.dtype or v.dtype != q.dtype:
@@ -135,10 +138,18 @@ def ring_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, C: int =
                                      seq_offsets is not None, dt)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    st = lib().ring_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), T_q, S_kv, h_q, h_kv, d, C,
-                             int(causal), _ptr(seq_offsets), n_seqs, dt,
-                             _ptr(workspace) if need else None, need, _stream(dev))
-    _check("ring_attn_fwd", st)
+    if window is None:
+        st = lib().ring_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), T_q, S_kv, h_q, h_kv, d, C,
+                                 int(causal), _ptr(seq_offsets), n_seqs, dt,
+                                 _ptr(workspace) if need else None, need, _stream(dev))
+        _check("ring_attn_fwd", st)
+    else:
+        if not causal:
+            raise ValueError("a sliding window needs causal=True")
+        st = lib().ring_attn_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), T_q, S_kv, h_q, h_kv, d, C,
+                                        int(window), _ptr(seq_offsets), n_seqs, dt,
+                                        _ptr(workspace) if need else None, need, _stream(dev))
+        _check("ring_attn_fwd_window", st)
     return o
 
 

@@ -145,9 +145,92 @@ hipError_t ensure_lds_limit(const void* fn, int bytes, std::atomic<unsigned>& do
 
 }  // namespace fakv
 
+static fakv_status ring_attn_impl(const void* q, const void* k, const void* v, void* o, int T_q, int S_kv,
+                                  int h_q, int h_kv, int d, int C, int causal, int window,
+                                  const int32_t* seq_offsets, int n_seqs, int dtype, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  fakv_status s = check_prefill_common(q, k, v, h_q, h_kv, d, dtype);
+  if (s != FAKV_OK) return s;
+  if (!o) return fail(FAKV_EINVAL, "o must be non-null");
+  if (!aligned16(o)) return fail(FAKV_EINVAL, "o must be 16-byte aligned");
+  if (T_q < 0 || S_kv < 0) return fail(FAKV_EINVAL, "T_q and S_kv must be >= 0");
+  if (C < 1) return fail(FAKV_EINVAL, "C must be >= 1 (got %d)", C);
+  if (n_seqs < 0 || (seq_offsets == nullptr && n_seqs < 1))
+    return fail(FAKV_EINVAL, "n_seqs must be >= 1 for a dense batch (got %d)", n_seqs);
+  const bool jagged = seq_offsets != nullptr;
+  const int BQ = query_tile(h_q, h_kv, d, dtype);
+  const int qh = dtype == FAKV_BF16 ? heads_per_wg(h_q, h_kv) : 1;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!jagged) {
+    if (S_kv % C) return fail(FAKV_EINVAL, "S_kv (%d) must be a multiple of C (%d)", S_kv, C);
+    if (causal && T_q != S_kv) return fail(FAKV_EINVAL, "causal attention needs T_q == S_kv (got %d, %d)", T_q, S_kv);
+    if (T_q > 0 && S_kv == 0) return fail(FAKV_EINVAL, "queries without keys: attention is undefined");
+    if ((long long)n_seqs * T_q * h_q * d >= (1ll << 40) || (long long)n_seqs * S_kv * h_kv * d >= (1ll << 40))
+      return fail(FAKV_EINVAL, "tensor too large");
+    if ((long long)n_seqs * T_q >= (1ll << 31) || (long long)n_seqs * S_kv >= (1ll << 31))
+      return fail(FAKV_EINVAL, "token count exceeds int32");
+    if ((s = check_kv_extent(S_kv, h_kv, d, dtype)) != FAKV_OK) return s;
+    if (T_q == 0) return FAKV_OK;
+    fakv::PrefillParams p = base_params(q, k, v, h_q, h_kv, d);
+    p.o = static_cast<uint16_t*>(o);
+    p.mode = 0;
+    p.n_seqs = n_seqs; p.T_q = T_q; p.S_kv = S_kv;
+    p.C = C; p.causal = causal ? 1 : 0;
+    p.window = window;
+    p.n_qtiles = (T_q + BQ - 1) / BQ;
+    p.n_hg = h_q / qh;
+    const long long grid = (long long)p.n_qtiles * p.n_hg * n_seqs;
+    if (grid > 0x7fffffffll) return fail(FAKV_EINVAL, "grid too large");
+    return launch_prefill(p, d, dtype, (int)grid, st);
+  }
+  // jagged batch
+  if (T_q != S_kv) return fail(FAKV_EINVAL, "a jagged batch needs T_q == S_kv == total tokens");
+  if (n_seqs < 1) return fail(FAKV_EINVAL, "a jagged batch needs n_seqs >= 1");
+  if (reinterpret_cast<uintptr_t>(seq_offsets) & 3u)
+    return fail(FAKV_EINVAL, "seq_offsets must be 4-byte aligned");
+  if ((long long)T_q * h_q * d >= (1ll << 40)) return fail(FAKV_EINVAL, "tensor too large");
+  if ((s = check_kv_extent(S_kv, h_kv, d, dtype)) != FAKV_OK) return s;
+  const size_t need = ring_attn_workspace_bytes(T_q, S_kv, h_q, h_kv, d, C, causal, n_seqs, 1, dtype);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(FAKV_EINVAL, "workspace too small: need %zu bytes, got %zu", need, workspace_bytes);
+  if (!aligned16(workspace)) return fail(FAKV_EINVAL, "workspace must be 16-byte aligned");
+  const bool bf16 = dtype == FAKV_BF16;
+  const int n_hg = h_q / qh;
+  const JaggedLayout L = jagged_layout(T_q, n_seqs, BQ, n_hg, bf16);
+  const size_t cap = L.cap;
+  if (cap > 0x7fffffffull || (long long)cap * n_hg > 0x7fffffffll) return fail(FAKV_EINVAL, "grid too large");
+  char* ws = static_cast<char*>(workspace);
+  int32_t* n_items = reinterpret_cast<int32_t*>(ws);
+  int32_t* items = reinterpret_cast<int32_t*>(ws + L.items);
+  hipError_t e = fakv::launch_worklist(seq_offsets, n_seqs, T_q, BQ, items, n_items, (int)cap, st);
+  if (e != hipSuccess) return device_fail("worklist launch", e);
+  fakv::PrefillParams p = base_params(q, k, v, h_q, h_kv, d);
+  p.o = static_cast<uint16_t*>(o);
+  p.mode = 0;
+  p.n_seqs = n_seqs; p.T_q = T_q; p.S_kv = S_kv;
+  p.C = C; p.causal = causal ? 1 : 0;
+  p.window = window;
+  p.items = items; p.n_items = n_items;
+  p.n_hg = n_hg;
+  if (!bf16) return launch_prefill(p, d, dtype, (int)(cap * n_hg), st);
+  fakv::SchedBufs sb;
+  sb.qinfo = reinterpret_cast<int32_t*>(ws + 64);
+  sb.nat2canon = reinterpret_cast<int32_t*>(ws + L.nat2canon);
+  sb.ntprefix = reinterpret_cast<int32_t*>(ws + L.ntprefix);
+  sb.seq_of_rank = reinterpret_cast<int32_t*>(ws + L.seq_of_rank);
+  sb.sched = reinterpret_cast<int32_t*>(ws + L.sched);
+  sb.stride = (int)L.stride;
+  e = fakv::launch_schedule(seq_offsets, n_seqs, BQ, items, n_items, n_hg, sb, st);
+  if (e != hipSuccess) return device_fail("schedule launch", e);
+  p.sched = sb.sched;
+  p.sched_stride = sb.stride;
+  p.qinfo = sb.qinfo;
+  return launch_prefill(p, d, dtype, fakv::prefill_bf16_persistent_grid(d, qh), st);
+}
+
 extern "C" {
 
-int fakv_abi_version(void) { return 100; }
+int fakv_abi_version(void) { return 101; }
 
 const char* fakv_last_error(void) { return g_err.c_str(); }
 
@@ -222,81 +305,18 @@ fakv_status ring_attn_fwd(const void* q, const void* k, const void* v, void* o, 
                           int n_seqs, int dtype, void* workspace, size_t workspace_bytes,
                           void* stream) {
   g_err.clear();
-  fakv_status s = check_prefill_common(q, k, v, h_q, h_kv, d, dtype);
-  if (s != FAKV_OK) return s;
-  if (!o) return fail(FAKV_EINVAL, "o must be non-null");
-  if (!aligned16(o)) return fail(FAKV_EINVAL, "o must be 16-byte aligned");
-  if (T_q < 0 || S_kv < 0) return fail(FAKV_EINVAL, "T_q and S_kv must be >= 0");
-  if (C < 1) return fail(FAKV_EINVAL, "C must be >= 1 (got %d)", C);
-  if (n_seqs < 0 || (seq_offsets == nullptr && n_seqs < 1))
-    return fail(FAKV_EINVAL, "n_seqs must be >= 1 for a dense batch (got %d)", n_seqs);
-  const bool jagged = seq_offsets != nullptr;
-  const int BQ = query_tile(h_q, h_kv, d, dtype);
-  const int qh = dtype == FAKV_BF16 ? heads_per_wg(h_q, h_kv) : 1;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (!jagged) {
-    if (S_kv % C) return fail(FAKV_EINVAL, "S_kv (%d) must be a multiple of C (%d)", S_kv, C);
-    if (causal && T_q != S_kv) return fail(FAKV_EINVAL, "causal attention needs T_q == S_kv (got %d, %d)", T_q, S_kv);
-    if (T_q > 0 && S_kv == 0) return fail(FAKV_EINVAL, "queries without keys: attention is undefined");
-    if ((long long)n_seqs * T_q * h_q * d >= (1ll << 40) || (long long)n_seqs * S_kv * h_kv * d >= (1ll << 40))
-      return fail(FAKV_EINVAL, "tensor too large");
-    if ((long long)n_seqs * T_q >= (1ll << 31) || (long long)n_seqs * S_kv >= (1ll << 31))
-      return fail(FAKV_EINVAL, "token count exceeds int32");
-    if ((s = check_kv_extent(S_kv, h_kv, d, dtype)) != FAKV_OK) return s;
-    if (T_q == 0) return FAKV_OK;
-    fakv::PrefillParams p = base_params(q, k, v, h_q, h_kv, d);
-    p.o = static_cast<uint16_t*>(o);
-    p.mode = 0;
-    p.n_seqs = n_seqs; p.T_q = T_q; p.S_kv = S_kv;
-    p.C = C; p.causal = causal ? 1 : 0;
-    p.n_qtiles = (T_q + BQ - 1) / BQ;
-    p.n_hg = h_q / qh;
-    const long long grid = (long long)p.n_qtiles * p.n_hg * n_seqs;
-    if (grid > 0x7fffffffll) return fail(FAKV_EINVAL, "grid too large");
-    return launch_prefill(p, d, dtype, (int)grid, st);
-  }
-  // jagged batch
-  if (T_q != S_kv) return fail(FAKV_EINVAL, "a jagged batch needs T_q == S_kv == total tokens");
-  if (n_seqs < 1) return fail(FAKV_EINVAL, "a jagged batch needs n_seqs >= 1");
-  if (reinterpret_cast<uintptr_t>(seq_offsets) & 3u)
-    return fail(FAKV_EINVAL, "seq_offsets must be 4-byte aligned");
-  if ((long long)T_q * h_q * d >= (1ll << 40)) return fail(FAKV_EINVAL, "tensor too large");
-  if ((s = check_kv_extent(S_kv, h_kv, d, dtype)) != FAKV_OK) return s;
-  const size_t need = ring_attn_workspace_bytes(T_q, S_kv, h_q, h_kv, d, C, causal, n_seqs, 1, dtype);
-  if (workspace == nullptr || workspace_bytes < need)
-    return fail(FAKV_EINVAL, "workspace too small: need %zu bytes, got %zu", need, workspace_bytes);
-  if (!aligned16(workspace)) return fail(FAKV_EINVAL, "workspace must be 16-byte aligned");
-  const bool bf16 = dtype == FAKV_BF16;
-  const int n_hg = h_q / qh;
-  const JaggedLayout L = jagged_layout(T_q, n_seqs, BQ, n_hg, bf16);
-  const size_t cap = L.cap;
-  if (cap > 0x7fffffffull || (long long)cap * n_hg > 0x7fffffffll) return fail(FAKV_EINVAL, "grid too large");
-  char* ws = static_cast<char*>(workspace);
-  int32_t* n_items = reinterpret_cast<int32_t*>(ws);
-  int32_t* items = reinterpret_cast<int32_t*>(ws + L.items);
-  hipError_t e = fakv::launch_worklist(seq_offsets, n_seqs, T_q, BQ, items, n_items, (int)cap, st);
-  if (e != hipSuccess) return device_fail("worklist launch", e);
-  fakv::PrefillParams p = base_params(q, k, v, h_q, h_kv, d);
-  p.o = static_cast<uint16_t*>(o);
-  p.mode = 0;
-  p.n_seqs = n_seqs; p.T_q = T_q; p.S_kv = S_kv;
-  p.C = C; p.causal = causal ? 1 : 0;
-  p.items = items; p.n_items = n_items;
-  p.n_hg = n_hg;
-  if (!bf16) return launch_prefill(p, d, dtype, (int)(cap * n_hg), st);
-  fakv::SchedBufs sb;
-  sb.qinfo = reinterpret_cast<int32_t*>(ws + 64);
-  sb.nat2canon = reinterpret_cast<int32_t*>(ws + L.nat2canon);
-  sb.ntprefix = reinterpret_cast<int32_t*>(ws + L.ntprefix);
-  sb.seq_of_rank = reinterpret_cast<int32_t*>(ws + L.seq_of_rank);
-  sb.sched = reinterpret_cast<int32_t*>(ws + L.sched);
-  sb.stride = (int)L.stride;
-  e = fakv::launch_schedule(seq_offsets, n_seqs, BQ, items, n_items, n_hg, sb, st);
-  if (e != hipSuccess) return device_fail("schedule launch", e);
-  p.sched = sb.sched;
-  p.sched_stride = sb.stride;
-  p.qinfo = sb.qinfo;
-  return launch_prefill(p, d, dtype, fakv::prefill_bf16_persistent_grid(d, qh), st);
+  return ring_attn_impl(q, k, v, o, T_q, S_kv, h_q, h_kv, d, C, causal, 0, seq_offsets, n_seqs, dtype,
+                        workspace, workspace_bytes, stream);
+}
+
+fakv_status ring_attn_fwd_window(const void* q, const void* k, const void* v, void* o, int T_q, int S_kv,
+                                 int h_q, int h_kv, int d, int C, int window, const int32_t* seq_offsets,
+                                 int n_seqs, int dtype, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  g_err.clear();
+  if (window < 1) return fail(FAKV_EINVAL, "window must be >= 1 (got %d)", window);
+  return ring_attn_impl(q, k, v, o, T_q, S_kv, h_q, h_kv, d, C, 1, window, seq_offsets, n_seqs, dtype,
+                        workspace, workspace_bytes, stream);
 }
 
 fakv_status splitkv_decode(const void* q, const void* k, const void* v, void* o, int B, int h_q,

@@ -173,6 +173,7 @@ struct KvWalk {
   int causal;
   int prune;
   int BK;
+  int lo;         // sliding window: first key the tile's first row admits (else very negative)
   // state
   int s;          // ring step of the current chunk
   int c0, c1;     // current chunk's key range
@@ -188,8 +189,10 @@ struct KvWalk {
     c1 = min(c0 + w, S);
     if (causal && prune) end = min(c1, q_hi + delta);
     else end = c1;
+    // dependent lower bound: start at the tile (on the chunk's grid) holding lo
     kt = c0;
-    return end > c0;
+    if (lo > c0) kt = c0 + ((lo - c0) / BK) * BK;
+    return end > kt;
   }
   __device__ __forceinline__ void first() {
     s = 0;

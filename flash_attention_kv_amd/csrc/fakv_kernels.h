@@ -33,6 +33,7 @@ struct PrefillParams {
   int n_hg;                // workgroups per query tile = h_q / heads per workgroup
   float scale;             // 1 / sqrt(d)
   float scale_log2;        // scale * log2(e)
+  int window;              // causal sliding window in keys (query i sees i - window < j <= i); 0 = none
 };
 
 struct DecodeParams {

@@ -93,6 +93,10 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
   walk.r = (Lq > 0) ? (int)(((long long)q_lo * p.C) / Lq) : 0;
   walk.q_hi = q_hi; walk.delta = delta; walk.causal = p.causal; walk.prune = p.prune;
   walk.BK = BK;
+  // sliding window W (causal): key j is admissible for query i iff
+  // i - W < j <= i; the walk starts at the tile holding the first row's first key
+  const int win = p.causal ? p.window : 0;
+  walk.lo = (win > 0 && p.prune) ? q_lo + delta - win + 1 : -(1 << 30);
   walk.first();
 
   // ---- query rows of this wave, resident as MFMA B operands ---------------
@@ -204,7 +208,8 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
     nxt.next();
     if (nxt.valid) issue_tile(nxt.kt, BUF ^ 1);
 
-    const bool skip = !wave_active || (p.causal && p.prune && kt > qw_hi - 1 + delta);
+    const bool skip = !wave_active || (p.causal && p.prune && kt > qw_hi - 1 + delta) ||
+                      (win > 0 && p.prune && kt + BK - 1 < qw_lo + delta - win + 1);
     // (d = 256 keeps the builtin reads: the extra staging registers of the
     // asm path push it into spills.)
     if constexpr (D <= 128) {
@@ -262,7 +267,8 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
       };
       issue_v(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
       // element mask only on tiles that cross the tail or the diagonal
-      const bool need_mask = (kt + BK > end) || (p.causal && (kt + BK - 1 > qw_lo + delta));
+      const bool need_mask = (kt + BK > end) || (p.causal && (kt + BK - 1 > qw_lo + delta)) ||
+                             (win > 0 && kt < qw_hi - 1 + delta - win + 1);
       if (need_mask) {
         const int qlim = qi + delta;
 #pragma unroll
@@ -270,7 +276,7 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = kt + 32 * b + 8 * (r >> 2) + 4 * half + (r & 3);
-            const bool ok = key < end && (!p.causal || key <= qlim);
+            const bool ok = key < end && (!p.causal || key <= qlim) && (win == 0 || key > qlim - win);
             if (!ok) sacc[b][r] = neg_inf();
           }
       }
@@ -344,7 +350,8 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
         }
       }
       // element mask only on tiles that cross the tail or the diagonal
-      const bool need_mask = (kt + BK > end) || (p.causal && (kt + BK - 1 > qw_lo + delta));
+      const bool need_mask = (kt + BK > end) || (p.causal && (kt + BK - 1 > qw_lo + delta)) ||
+                             (win > 0 && kt < qw_hi - 1 + delta - win + 1);
       if (need_mask) {
         const int qlim = qi + delta;
 #pragma unroll
@@ -352,7 +359,7 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = kt + 32 * b + 8 * (r >> 2) + 4 * half + (r & 3);
-            const bool ok = key < end && (!p.causal || key <= qlim);
+            const bool ok = key < end && (!p.causal || key <= qlim) && (win == 0 || key > qlim - win);
             if (!ok) sacc[b][r] = neg_inf();
           }
       }

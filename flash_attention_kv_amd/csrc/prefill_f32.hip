@@ -66,6 +66,10 @@ void prefill_f32_kernel(PrefillParams p) {
   walk.r = (Lq > 0) ? (int)(((long long)q_lo * p.C) / Lq) : 0;
   walk.q_hi = q_hi; walk.delta = delta; walk.causal = p.causal; walk.prune = p.prune;
   walk.BK = BK;
+  // sliding window W (causal): key j is admissible for query i iff
+  // i - W < j <= i; the walk starts at the tile holding the first row's first key
+  const int win = p.causal ? p.window : 0;
+  walk.lo = (win > 0 && p.prune) ? q_lo + delta - win + 1 : -(1 << 30);
   walk.first();
 
   const int qw_lo = q_lo + 32 * wave;
@@ -136,19 +140,22 @@ void prefill_f32_kernel(PrefillParams p) {
     nxt.next();
     if (nxt.valid) load_tile(nxt.kt, nxt.end);
 
-    const bool skip = !wave_active || (p.causal && p.prune && kt > qw_hi - 1 + delta);
+    const bool skip = !wave_active || (p.causal && p.prune && kt > qw_hi - 1 + delta) ||
+                      (win > 0 && p.prune && kt + BK - 1 < qw_lo + delta - win + 1);
     if (!skip) {
       const float* kl = reinterpret_cast<const float*>(smem + buf * (KBYTES + VBYTES));
       const float* vl = reinterpret_cast<const float*>(smem + buf * (KBYTES + VBYTES) + KBYTES);
       f32x16 sacc = f32x16{};
 #pragma unroll
       for (int s = 0; s < D / 2; ++s) sacc = mfma32x32x2f32(kl[col * KST + 2 * s + half], qreg[s], sacc);
-      const bool need_mask = (kt + BK > end) || (p.causal && (kt + BK - 1 > qw_lo + delta));
+      const bool need_mask = (kt + BK > end) || (p.causal && (kt + BK - 1 > qw_lo + delta)) ||
+                             (win > 0 && kt < qw_hi - 1 + delta - win + 1);
       if (need_mask) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kt + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (!(key < end && (!p.causal || key <= qi + delta))) sacc[r] = neg_inf();
+          if (!(key < end && (!p.causal || key <= qi + delta) && (win == 0 || key > qi + delta - win)))
+            sacc[r] = neg_inf();
         }
       }
       float mt = neg_inf();

@@ -133,6 +133,23 @@ fakv_status ring_attn_fwd(const void* q, const void* k, const void* v, void* o,
                           const int32_t* seq_offsets, int n_seqs, int dtype,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * ring_attn_fwd_window -- causal prefill restricted to a sliding window.
+ *
+ * As ring_attn_fwd with causal = 1, except that query i of a sequence sees
+ * only keys i - window < j <= i (local positions): the dependent *lower*
+ * bound that the Helion page ("Scalar minimum") leaves to sliding-window
+ * support.  The KV walk of a query tile starts at the tile holding
+ * max(chunk start, tile start - window + 1), chunks wholly below it are
+ * skipped, and only tiles crossing either edge of the band are masked.
+ * window >= the sequence length gives plain causal attention.  Same layouts,
+ * workspace and errors as ring_attn_fwd; window < 1 is FAKV_EINVAL.
+ */
+fakv_status ring_attn_fwd_window(const void* q, const void* k, const void* v, void* o,
+                                 int T_q, int S_kv, int h_q, int h_kv, int d, int C, int window,
+                                 const int32_t* seq_offsets, int n_seqs, int dtype,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace needed by ring_attn_fwd for these arguments (jagged = seq_offsets
  * != NULL).  0 for dense batches. */
 size_t ring_attn_workspace_bytes(int T_q, int S_kv, int h_q, int h_kv, int d, int C,
@@ -184,7 +201,7 @@ int fakv_query_tile_rows(int h_q, int h_kv, int d, int dtype);
  * Valid until the next library call on that thread. */
 const char* fakv_last_error(void);
 
-/* ABI version of this header (major * 100 + minor). */
+/* ABI version of this header (major * 100 + minor): 101. */
 int fakv_abi_version(void);
 
 #ifdef __cplusplus

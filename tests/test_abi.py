@@ -31,7 +31,7 @@ def test_header_symbols_exported():
 
 def test_version_and_tile_rows():
     L = F.lib()
-    assert L.fakv_abi_version() == 100
+    assert L.fakv_abi_version() == 101
     assert F.query_tile_rows(32, 8, 128) == 32      # 4 query heads share a KV tile
     assert F.query_tile_rows(32, 32, 256) == 128
     assert F.query_tile_rows(6, 3, 64) == 64
@@ -107,3 +107,13 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         B.lib()
+
+
+def test_window_entry_rejects():
+    L = F.lib()
+    # sliding window: window >= 1, and the ring_attn_fwd checks apply
+    assert L.ring_attn_fwd_window(16, 16, 16, 16, 8, 8, 4, 2, 128, 1, 0, None, 1, F.BF16, None, 0, None) == EINVAL
+    assert b"window" in L.fakv_last_error()
+    assert L.ring_attn_fwd_window(16, 16, 16, 16, 8, 16, 4, 2, 128, 1, 4, None, 1, F.BF16, None, 0, None) == EINVAL
+    assert b"T_q == S_kv" in L.fakv_last_error()
+    assert L.ring_attn_fwd_window(16, 16, 16, 16, 0, 0, 4, 2, 128, 1, 4, None, 1, F.BF16, None, 0, None) == 0

@@ -17,6 +17,9 @@ Workloads (shapes follow the pages' problems; all values are i.i.d. N(0, 1)):
   causal self-attn"): 1152 sequences, 4 heads, d = 128, bf16.  The page does
   not give its length distribution; lengths are drawn uniformly from
   [64, 2048] with numpy's PCG64 seeded 0.
+* ``gqa_swa``     -- the ``gqa_ring`` shape with a causal sliding window of 2048
+  keys (the dependent lower bound the Helion page defers to sliding-window
+  support), seed 6.
 * ``decode``      -- split-KV GQA decode in the shape of the mesh decode page's
   headline scale: 8 sequences, 64 query heads over 8 KV heads, d = 128,
   131072 cached keys per sequence in 64 chunks, bf16.
@@ -49,6 +52,7 @@ class Workload:
     C: int = 1
     causal: bool = False
     jagged: bool = False
+    window: Optional[int] = None   # causal sliding window (keys), None = none
     # decode
     B: int = 0
     S_cache: int = 0
@@ -65,6 +69,8 @@ WORKLOADS = {
                              n_seqs=8, T_q=4096, S_kv=4096, C=1, causal=True),
     "jagged": Workload("jagged", "prefill", "bf16", h_q=4, h_kv=4, d=128, seed=4,
                        n_seqs=1152, C=1, causal=True, jagged=True),
+    "gqa_swa": Workload("gqa_swa", "prefill", "bf16", h_q=32, h_kv=8, d=128, seed=6,
+                        T_q=8192, S_kv=8192, C=8, causal=True, window=2048),
     "decode": Workload("decode", "decode", "bf16", h_q=64, h_kv=8, d=128, seed=5,
                        B=8, S_cache=131072, n_chunks=64),
 }
