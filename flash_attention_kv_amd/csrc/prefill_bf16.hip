@@ -7,11 +7,16 @@
 // inside a chunk, the tiles of BK keys up to the dependent end
 // min(chunk end, query tile end) ("[pallas] Support dependent Tile.end bounds
 // in Pallas", "Unroll lowering": the trip count shrinks instead of masking
-// whole tiles).  Per tile:
+// whole tiles).  With a sliding window W the walk also starts late: at the
+// tile holding max(chunk start, query tile start - W + 1) (the dependent
+// lower bound the same page's "Scalar minimum" section leaves to
+// sliding-window support).  Per tile:
 //   1. K and V tiles go HBM -> LDS directly (buffer_load_dwordx4 ... lds: no
 //      register staging), double-buffered: tile t+1 is in flight while tile t
 //      computes.  Keys past the tile's valid end are masked.
-//   2. S^T = K Q^T on MFMA (Q resident in registers as the B operand).
+//   2. S^T = K Q^T on MFMA (Q resident in registers as the B operand); for
+//      d <= 128 the LDS operand reads are inline asm with explicit lgkmcnt
+//      waits so that the prefetch of tile t+1 is not waited for early.
 //   3. The online-softmax fold of the prefill page's ring step, with the
 //      block partial folded directly into the running (m, l, O): row max,
 //      exp2 of pre-scaled scores, per-lane partial row sums.  l and O are
@@ -21,8 +26,9 @@
 //      V^T read from the row-major V tile with the LDS transpose read
 //      ds_read_b64_tr_b16 (a 16-lane group turns 4 keys x 16 dims into
 //      16 dims x 4 keys).
-// Only tiles that straddle the diagonal or the chunk's tail evaluate the
-// element mask.  The epilogue writes O / l in bf16, or the fp32 triplet.
+// Only tiles that straddle the diagonal, a window edge or the chunk's tail
+// evaluate the element mask.  The epilogue writes O / l in bf16, or the fp32
+// triplet.
 #include <type_traits>
 
 #include "fakv_device.h"
