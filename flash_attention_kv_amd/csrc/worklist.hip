@@ -22,18 +22,24 @@ namespace fakv {
 __global__ __launch_bounds__(1024)
 void worklist_kernel(const int32_t* __restrict__ off, int n_seqs, int total, int BQ,
                      int32_t* __restrict__ items, int32_t* __restrict__ n_items, int capacity) {
+  constexpr int kCache = 8192;         // lengths of the first sequences, kept in LDS
   __shared__ int s_wave[16];
   __shared__ int s_max;
   __shared__ int s_bad;
+  __shared__ int s_len[kCache];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) { s_max = 0; s_bad = (off[0] != 0 || off[n_seqs] != total) ? 1 : 0; }
   __syncthreads();
   int local_max = 0, bad = 0;
   for (int b = tid; b < n_seqs; b += 1024) {
     const int L = off[b + 1] - off[b];
+    if (b < kCache) s_len[b] = L;
     if (L < 0) bad = 1;
     local_max = max(local_max, (max(L, 0) + BQ - 1) / BQ);
   }
+  // the ranking passes below revisit every sequence once per tile index:
+  // lengths come from LDS, not from global offsets, on that path
+  auto len = [&](int b) { return b < kCache ? s_len[b] : off[b + 1] - off[b]; };
   if (bad) atomicOr(&s_bad, 1);
   atomicMax(&s_max, local_max);
   __syncthreads();
@@ -47,7 +53,7 @@ void worklist_kernel(const int32_t* __restrict__ off, int n_seqs, int total, int
     for (int b0 = 0; b0 < n_seqs; b0 += 1024) {
       const int b = b0 + tid;
       int L = 0;
-      if (b < n_seqs) L = off[b + 1] - off[b];
+      if (b < n_seqs) L = len(b);
       const bool flag = b < n_seqs && L > t * BQ;
       const unsigned long long bal = __ballot(flag);
       const int below = __popcll(bal & ((1ull << lane) - 1ull));
@@ -85,15 +91,69 @@ void worklist_kernel(const int32_t* __restrict__ off, int n_seqs, int total, int
 // first -- are contiguous in its queue, so the workgroups that take them run
 // at the same time on one XCD and share that sequence's K/V in its L2.
 // Entry = record index * n_hg + head group.  Runs after worklist_kernel on
-// the same stream; an empty worklist gives empty queues.
+// the same stream; an empty worklist gives empty queues.  The order among
+// sequences of equal tile count is whatever the LDS atomics produce: it only
+// decides which workgroup computes an item, never a result.
+
+// Exclusive prefix sum over the 1024 threads of the block: wave scans with
+// lane shuffles, then one pass over the 16 wave totals.  Returns the block
+// total; uses two barriers.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) s_wave[wave] = x;
+  __syncthreads();
+  int pre = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    const int c = s_wave[w];
+    pre += (w < wave) ? c : 0;
+    total += c;
+  }
+  __syncthreads();
+  return pre + x - v;
+}
+
+// Exclusive prefix sum over the threads of each residue class tid mod 8
+// (the 8 queues): lane shuffles by 8, 16, 32 inside a wave, then the earlier
+// waves' per-class totals.  Returns the class total of the block in total.
+__device__ __forceinline__ int block_exclusive_scan8(int v, int* s_w8, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, x8 = threadIdx.x & 7;
+  int x = v;
+#pragma unroll
+  for (int d = 8; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane >= 56) s_w8[wave * 8 + x8] = x;
+  __syncthreads();
+  int pre = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    const int c = s_w8[w * 8 + x8];
+    pre += (w < wave) ? c : 0;
+    total += c;
+  }
+  __syncthreads();
+  return pre + x - v;
+}
+
 __global__ __launch_bounds__(1024)
 void schedule_kernel(const int32_t* __restrict__ off, int n_seqs, int BQ, const int32_t* __restrict__ items,
                      const int32_t* __restrict__ n_items_p, int n_hg, SchedBufs sb) {
-  __shared__ int s_val[1024];
   __shared__ int s_wave[16];
+  __shared__ int s_w8[128];
   __shared__ int s_carry[8];
-  __shared__ int s_misc[2];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ int s_max;
+  __shared__ int s_hist[1025];         // tile counts 1 .. 1024 (larger ones share the last bin)
+  const int tid = threadIdx.x;
   const int n_items = *n_items_p;
   if (n_items == 0) {          // empty batch or rejected offsets
     if (tid < 16) sb.qinfo[tid] = 0;
@@ -101,60 +161,73 @@ void schedule_kernel(const int32_t* __restrict__ off, int n_seqs, int BQ, const 
   }
   // (offsets are a valid prefix array here: worklist_kernel checked them)
   auto ntiles = [&](int b) { return (off[b + 1] - off[b] + BQ - 1) / BQ; };
+  auto bin = [&](int v) { return min(v, 1024); };
 
-  // 1. exclusive prefix sums of tiles per sequence
-  if (tid == 0) { s_misc[0] = 0; s_misc[1] = 0; }
+  // 1. exclusive prefix sums of tiles per sequence; histogram of tile counts
+  for (int i = tid; i < 1025; i += 1024) s_hist[i] = 0;
+  if (tid == 0) s_max = 0;
   __syncthreads();
+  int carry = 0;
   for (int b0 = 0; b0 < n_seqs; b0 += 1024) {
     const int b = b0 + tid;
     const int v = b < n_seqs ? ntiles(b) : 0;
-    s_val[tid] = v;
-    __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {
-      const int t = tid >= d ? s_val[tid - d] : 0;
-      __syncthreads();
-      s_val[tid] += t;
-      __syncthreads();
+    int tot;
+    const int ex = block_exclusive_scan(v, s_wave, tot);
+    if (b < n_seqs) {
+      sb.ntprefix[b] = carry + ex;
+      if (v > 0) atomicAdd(&s_hist[bin(v)], 1);
     }
-    if (b < n_seqs) sb.ntprefix[b] = s_misc[0] + s_val[tid] - v;
-    atomicMax(&s_misc[1], v);
-    __syncthreads();
-    if (tid == 1023) s_misc[0] += s_val[1023];
-    __syncthreads();
+    carry += tot;
   }
-  if (tid == 0) sb.ntprefix[n_seqs] = s_misc[0];
-  const int T = s_misc[1];
-  __syncthreads();
+  if (tid == 0) sb.ntprefix[n_seqs] = carry;
+  __syncthreads();                     // prefix sums and histogram complete
 
   // 2. (sequence, tile) in natural order -> worklist record index
   for (int i = tid; i < n_items; i += 1024) {
     const int32_t* r = items + 8 * (size_t)i;
     sb.nat2canon[sb.ntprefix[r[0]] + r[1]] = i;
   }
+  __syncthreads();
 
-  // 3. rank sequences by tile count, descending, ties by index
-  int base = 0;
-  for (int v = T; v >= 1; --v) {
+  // 3. rank sequences by tile count, descending: start of each bin from the
+  //    top, then one slot per sequence by an atomic cursor in its bin.
+  //    Counts beyond 1024 tiles share the top bin; within it they are
+  //    ordered by a second, exact pass.
+  {
+    int v = 0;
+    if (tid < 1024) v = s_hist[1024 - tid];        // bins from the top: 1024, 1023, .. 1
+    int tot;
+    const int ex = block_exclusive_scan(v, s_wave, tot);
+    if (tid < 1024) s_hist[1024 - tid] = ex;      // now: first rank of the bin
+    __syncthreads();
     for (int b0 = 0; b0 < n_seqs; b0 += 1024) {
       const int b = b0 + tid;
-      const bool flag = b < n_seqs && ntiles(b) == v;
-      const unsigned long long bal = __ballot(flag);
-      const int below = __popcll(bal & ((1ull << lane) - 1ull));
-      if (lane == 0) s_wave[wave] = __popcll(bal);
-      __syncthreads();
-      int pre = 0, tot = 0;
-      for (int w = 0; w < 16; ++w) {
-        const int c = s_wave[w];
-        pre += (w < wave) ? c : 0;
-        tot += c;
+      if (b < n_seqs) {
+        const int nt = ntiles(b);
+        if (nt > 0) sb.seq_of_rank[atomicAdd(&s_hist[bin(nt)], 1)] = b;
       }
-      if (flag) sb.seq_of_rank[base + pre + below] = b;
-      base += tot;
-      __syncthreads();
+    }
+    if (tid == 0) s_max = tot;                     // non-empty sequences
+    __syncthreads();
+  }
+  const int n_ranked = s_max;
+  // sequences with more than 1024 tiles: order the top bin exactly (rare)
+  if (s_hist[1024] > 0) {
+    // top bin occupies ranks [0, n_big); sort it by count, descending (one thread)
+    if (tid == 0) {
+      int n_big = 0;
+      while (n_big < n_ranked && ntiles(sb.seq_of_rank[n_big]) >= 1024) ++n_big;
+      for (int i = 1; i < n_big; ++i) {
+        const int x = sb.seq_of_rank[i];
+        const int vx = ntiles(x);
+        int j = i - 1;
+        while (j >= 0 && ntiles(sb.seq_of_rank[j]) < vx) { sb.seq_of_rank[j + 1] = sb.seq_of_rank[j]; --j; }
+        sb.seq_of_rank[j + 1] = x;
+      }
     }
   }
-  const int n_units = base * n_hg;     // non-empty sequences x head groups
-  __syncthreads();                     // seq_of_rank and nat2canon complete
+  __syncthreads();
+  const int n_units = n_ranked * n_hg;   // non-empty sequences x head groups
 
   // 4. deal units onto the queues; per-queue offsets by a stride-8 scan
   if (tid < 8) s_carry[tid] = 0;
@@ -167,22 +240,16 @@ void schedule_kernel(const int32_t* __restrict__ off, int n_seqs, int BQ, const 
     const int b = valid ? sb.seq_of_rank[r] : 0;
     const int v = valid ? ntiles(b) : 0;
     const int x = tid & 7;             // == k mod 8 since k0 is a multiple of 1024
-    s_val[tid] = v;
-    __syncthreads();
-    for (int d = 8; d < 1024; d <<= 1) {
-      const int t = tid >= d ? s_val[tid - d] : 0;
-      __syncthreads();
-      s_val[tid] += t;
-      __syncthreads();
-    }
+    int tot;
+    const int ex = block_exclusive_scan8(v, s_w8, tot);
     if (valid) {
-      const int pos = s_carry[x] + s_val[tid] - v;
+      const int pos = s_carry[x] + ex;
       int32_t* q = sb.sched + (size_t)x * sb.stride + pos;
       const int32_t* nc = sb.nat2canon + sb.ntprefix[b];
       for (int j = 0; j < v; ++j) q[j] = nc[v - 1 - j] * n_hg + hg;
     }
     __syncthreads();
-    if (tid >= 1016) s_carry[x] += s_val[tid];
+    if (tid < 8) s_carry[tid] += tot;
     __syncthreads();
   }
   if (tid < 8) sb.qinfo[tid] = s_carry[tid];
