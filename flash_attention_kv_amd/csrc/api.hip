@@ -43,9 +43,11 @@ int heads_per_wg(int h_q, int h_kv) {
   return (g % 4 == 0) ? 4 : (g % 2 == 0) ? 2 : 1;
 }
 
-int query_tile(int h_q, int h_kv, int d, int dtype) {
+// Query rows per workgroup tile; bf16 jagged batches use taller tiles than
+// dense ones (more waves share each K/V tile in LDS).
+int query_tile(int h_q, int h_kv, int d, int dtype, bool jagged) {
   if (dtype == FAKV_F32) return fakv::kF32QueryTile;
-  return fakv::prefill_bf16_query_rows(d, heads_per_wg(h_q, h_kv));
+  return fakv::prefill_bf16_query_rows(d, heads_per_wg(h_q, h_kv), jagged);
 }
 
 bool env_no_prune() {
@@ -158,7 +160,7 @@ static fakv_status ring_attn_impl(const void* q, const void* k, const void* v, v
   if (n_seqs < 0 || (seq_offsets == nullptr && n_seqs < 1))
     return fail(FAKV_EINVAL, "n_seqs must be >= 1 for a dense batch (got %d)", n_seqs);
   const bool jagged = seq_offsets != nullptr;
-  const int BQ = query_tile(h_q, h_kv, d, dtype);
+  const int BQ = query_tile(h_q, h_kv, d, dtype, jagged);
   const int qh = dtype == FAKV_BF16 ? heads_per_wg(h_q, h_kv) : 1;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (!jagged) {
@@ -236,14 +238,14 @@ const char* fakv_last_error(void) { return g_err.c_str(); }
 
 int fakv_query_tile_rows(int h_q, int h_kv, int d, int dtype) {
   if (h_q < 1 || h_kv < 1 || h_q % h_kv || !supported_d(d)) return 0;
-  return query_tile(h_q, h_kv, d, dtype);
+  return query_tile(h_q, h_kv, d, dtype, true);
 }
 
 size_t ring_attn_workspace_bytes(int T_q, int S_kv, int h_q, int h_kv, int d, int C, int causal,
                                  int n_seqs, int jagged, int dtype) {
   (void)S_kv; (void)C; (void)causal;
   if (!jagged || T_q <= 0 || n_seqs < 1 || h_q < 1 || h_kv < 1 || h_q % h_kv || !supported_d(d)) return 0;
-  const int BQ = query_tile(h_q, h_kv, d, dtype);
+  const int BQ = query_tile(h_q, h_kv, d, dtype, true);
   const bool bf16 = dtype == FAKV_BF16;
   const int n_hg = bf16 ? h_q / heads_per_wg(h_q, h_kv) : h_q;
   return jagged_layout(T_q, n_seqs, BQ, n_hg, bf16).total;
@@ -275,7 +277,7 @@ fakv_status attn_partial(const void* q, const void* k, const void* v, float* m, 
   p.n_seqs = 1; p.T_q = T_q; p.S_kv = S_chunk;
   p.C = 1; p.causal = causal ? 1 : 0;
   p.q_pos0 = q_pos0; p.k_pos0 = k_pos0;
-  const int BQ = query_tile(h_q, h_kv, d, dtype);
+  const int BQ = query_tile(h_q, h_kv, d, dtype, false);
   const int qh = dtype == FAKV_BF16 ? heads_per_wg(h_q, h_kv) : 1;
   p.n_qtiles = (T_q + BQ - 1) / BQ;
   p.n_hg = h_q / qh;

@@ -61,8 +61,8 @@ struct MergeParams {
 hipError_t ensure_lds_limit(const void* fn, int bytes, std::atomic<unsigned>& done_mask);
 
 // Query rows of one bf16 workgroup tile for head dim d and qh query heads
-// per workgroup.
-int prefill_bf16_query_rows(int d, int qh);
+// per workgroup, for a dense or a jagged batch.
+int prefill_bf16_query_rows(int d, int qh, bool jagged);
 hipError_t launch_prefill_bf16(const PrefillParams& p, int d, int qh, int grid, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillParams& p, int d, int grid, hipStream_t stream);
 constexpr int kF32QueryTile = 128;   // query rows per fp32 workgroup

@@ -193,8 +193,9 @@ fakv_status fakv_jagged_worklist(const int32_t* seq_offsets, int n_seqs, int tot
                                  int BQ, int32_t* items, int32_t* n_items, size_t capacity,
                                  void* stream);
 
-/* Query-tile height ring_attn_fwd uses for these arguments (the BQ of its
- * worklist). */
+/* Query-tile height of the worklist ring_attn_fwd builds for a jagged batch
+ * with these arguments (its BQ; bf16 dense batches run tiles half as tall).
+ * 0 for arguments ring_attn_fwd rejects (h_q not a multiple of h_kv, d). */
 int fakv_query_tile_rows(int h_q, int h_kv, int d, int dtype);
 
 /* Message describing the last failure on the calling thread ("" if none).

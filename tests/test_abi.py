@@ -32,9 +32,11 @@ def test_header_symbols_exported():
 def test_version_and_tile_rows():
     L = F.lib()
     assert L.fakv_abi_version() == 101
-    assert F.query_tile_rows(32, 8, 128) == 32      # 4 query heads share a KV tile
-    assert F.query_tile_rows(32, 32, 256) == 128
-    assert F.query_tile_rows(6, 3, 64) == 64
+    # jagged bf16 tiles: 8 waves of 32 rows, split over the query heads that
+    # share a KV tile
+    assert F.query_tile_rows(32, 8, 128) == 64      # 4 query heads share a KV tile
+    assert F.query_tile_rows(32, 32, 256) == 256
+    assert F.query_tile_rows(6, 3, 64) == 128
     assert F.query_tile_rows(4, 4, 128, F.F32) == 128
     assert F.query_tile_rows(3, 2, 128) == 0
 
