@@ -254,7 +254,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(head["tflops"], 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(head["tflops"] / PEAK_BF16_TFLOPS, 4),
                      "traffic": load_traffic("gqa_ring"),
-                     "kernel": "prefill_bf16_kernel<128, 4> (d=128, 4 query heads per workgroup, 64-key tiles)", "useful_flops_per_launch": head["flops"]},
+                     "kernel": "prefill_bf16_kernel<128, 4, 4> (d=128, 4 query heads per 4-wave workgroup, 64-key tiles)", "useful_flops_per_launch": head["flops"]},
         "cpu_baseline": cpu,
         "extra": extra,
         "kernel_sources": csrc_hash(),
