@@ -119,3 +119,18 @@ def test_window_entry_rejects():
     assert L.ring_attn_fwd_window(16, 16, 16, 16, 8, 16, 4, 2, 128, 1, 4, None, 1, F.BF16, None, 0, None) == EINVAL
     assert b"T_q == S_kv" in L.fakv_last_error()
     assert L.ring_attn_fwd_window(16, 16, 16, 16, 0, 0, 4, 2, 128, 1, 4, None, 1, F.BF16, None, 0, None) == 0
+
+
+def test_kv_span_limit():
+    # one sequence's K (or V) span must stay below 2 GiB (the buffer resources
+    # that bound every tile load are 31-bit); 65535 keys x 64 heads x d = 256
+    # is the largest such span, one key more is refused before any HIP call
+    L = F.lib()
+    assert _ring(T_q=0, S_kv=65535, h_q=64, h_kv=64, d=256) == 0
+    assert _ring(T_q=0, S_kv=65536, h_q=64, h_kv=64, d=256) == EUNSUP
+    assert b"2 GiB" in L.fakv_last_error()
+    assert L.attn_partial(16, 16, 16, 16, 16, 16, 8, 65536, 64, 64, 256, 0, 0, 0, 0, F.BF16, None) == EUNSUP
+    assert b"2 GiB" in L.fakv_last_error()
+    ws = F.splitkv_decode_workspace_bytes(1, 64, 256, 64)
+    assert L.splitkv_decode(16, 16, 16, 16, 1, 64, 64, 256, 65536, 64, F.BF16, 16, ws, None) == EUNSUP
+    assert b"2 GiB" in L.fakv_last_error()
