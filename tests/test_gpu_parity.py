@@ -240,3 +240,28 @@ def test_jagged_many_sequences(heads):
     o = F.ring_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, seq_offsets=torch.from_numpy(offs).to(DEV))
     torch.cuda.synchronize()
     check(host(o), oracle.attention_ref(q, k, v, causal=True, seq_offsets=offs), "bf16", f"jagged many {heads}")
+
+
+@pytest.mark.parametrize("d,heads,C", [(64, (6, 2), 1), (64, (2, 2), 2), (256, (4, 2), 1), (256, (1, 1), 3)])
+def test_jagged_bf16_head_dims(d, heads, C):
+    """Jagged batches at the other head dims (the d = 64 and d = 256 tiles of
+    the 8-wave jagged kernel): ragged lengths around the 256- and 128-row
+    tiles, an empty sequence and a single token."""
+    h_q, h_kv = heads
+    lens = [257, 1, 0, 129, 512, 37]
+    offs = seq_offsets_from_lengths(lens)
+    N = int(offs[-1])
+    q, k, v = _qkv(N, N, h_q, h_kv, d, "bf16", N + d + C)
+    o = F.ring_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), C=C, causal=True,
+                        seq_offsets=torch.from_numpy(offs).to(DEV))
+    torch.cuda.synchronize()
+    check(host(o), oracle.ring_ref(q, k, v, C, causal=True, seq_offsets=offs), "bf16", f"jagged d={d} {heads} C={C}")
+
+
+@pytest.mark.parametrize("d,B,h_q,h_kv,S,n_chunks", [(64, 2, 16, 2, 1500, 9), (256, 1, 8, 8, 700, 5),
+                                                      (256, 2, 32, 1, 333, 3)])
+def test_splitkv_decode_head_dims(d, B, h_q, h_kv, S, n_chunks):
+    q, k, v = randn([(B, h_q, d), (B, S, h_kv, d), (B, S, h_kv, d)], d + S, "bf16")
+    o = F.splitkv_decode(q.to(DEV), k.to(DEV), v.to(DEV), n_chunks=n_chunks)
+    torch.cuda.synchronize()
+    check(host(o), oracle.splitkv_decode_ref(q, k, v, n_chunks), "bf16", f"decode d={d} B={B} h={h_q}/{h_kv}")
