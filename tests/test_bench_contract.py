@@ -1,0 +1,38 @@
+"""bench.py without a GPU: the multi-GPU refusal, and the rule that HBM traffic
+figures are reported only when they were measured on the current kernel
+sources."""
+import json
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert msg["n_gpus"] == 2 and "one GPU" in msg["error"]
+
+
+def test_traffic_follows_the_kernel_sources(tmp_path, monkeypatch):
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "profiles" / "traffic.json").write_text(json.dumps({
+        "gqa_ring": {"csrc_hash": "aaaa", "bytes_per_launch": 123},
+        "decode": {"csrc_hash": "bbbb", "bytes_per_launch": 456}}))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "csrc_hash", lambda: "aaaa")
+    assert bench.load_traffic("gqa_ring") == 123
+    assert bench.load_traffic("decode") is None          # taken on other sources
+    assert bench.load_traffic("jagged") is None          # never measured
+
+
+def test_source_hash_covers_every_kernel_file():
+    h = bench.csrc_hash()
+    assert len(h) == 16 and h == bench.csrc_hash()
+    srcs = sorted(os.listdir(os.path.join(ROOT, "flash_attention_kv_amd", "csrc")))
+    assert any(s.endswith(".hip") for s in srcs) and "fakv_device.h" in srcs
