@@ -118,7 +118,9 @@ fakv_status lse_merge(const float* m_parts, const float* l_parts, const float* o
  *   is split into C contiguous chunks of ceil(L_b / C) keys.  The offsets are
  *   read on the device only (no host synchronisation); a device-built
  *   (sequence, query-tile) worklist, longest tiles first, lives in the
- *   workspace.
+ *   workspace.  Offsets that are not such a prefix array are detected on the
+ *   device: the worklist comes out empty and o is left untouched (nothing is
+ *   read or written out of bounds).
  * Each query tile takes the ring position of its first row, r = floor(i*C/L),
  * and visits KV chunks in the order (r + s) mod C, s = 0..C-1, as the prefill
  * page's rank r does after s westward rotations.  Causal: a chunk starting at

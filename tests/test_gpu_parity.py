@@ -265,3 +265,17 @@ def test_splitkv_decode_head_dims(d, B, h_q, h_kv, S, n_chunks):
     o = F.splitkv_decode(q.to(DEV), k.to(DEV), v.to(DEV), n_chunks=n_chunks)
     torch.cuda.synchronize()
     check(host(o), oracle.splitkv_decode_ref(q, k, v, n_chunks), "bf16", f"decode d={d} B={B} h={h_q}/{h_kv}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("offs", [[0, 5, 3, 10], [0, 4, 9], [1, 4, 10]])
+def test_jagged_bad_offsets_leave_output_untouched(dtype, offs):
+    """Offsets that are not a prefix array of the T_q tokens (decreasing, last
+    != total, first != 0) give an empty worklist: no kernel writes o."""
+    N = 10
+    q, k, v = _qkv(N, N, 2, 1, 64, dtype, 5)
+    o = torch.full(q.shape, 7.0, dtype=q.dtype, device=DEV)
+    F.ring_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True,
+                    seq_offsets=torch.tensor(offs, dtype=torch.int32, device=DEV), out=o)
+    torch.cuda.synchronize()
+    assert bool((o == 7.0).all())
