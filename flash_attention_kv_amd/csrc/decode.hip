@@ -16,8 +16,8 @@
 //   V: 32 x d tiles go HBM -> LDS directly (buffer_load ... lds) into two
 //      wave-private stages, swizzled so that the A operand of O^T += V^T P^T
 //      is read with the conflict-free transpose read ds_read_b64_tr_b16.
-// Buffer resources span one (sequence, KV head)'s keys, so no load can leave
-// the cache tensors.  Each wave writes its unit's triplet: m, l
+// Buffer resources span one unit's keys (one chunk of one sequence and KV
+// head), so no load can leave the unit.  Each wave writes its unit's triplet: m, l
 // (n_chunks, B*h_q) and O unnormalised (n_chunks, B*h_q, d), the layout
 // lse_merge consumes.
 #include <type_traits>
@@ -70,8 +70,10 @@ void decode_partial_kernel(DecodeParams p, int g) {
   }
 
   const unsigned stride_b = (unsigned)p.h_kv * D * 2;
-  const size_t head_off = ((size_t)b * p.S * p.h_kv + kvh) * D;
-  const unsigned extent = (unsigned)(p.S - 1) * stride_b + D * 2;
+  // The resources span this unit's own keys [w0, w1) only: the loads issued
+  // past its last step read zeros without touching memory.
+  const size_t head_off = (((size_t)b * p.S + w0) * p.h_kv + kvh) * D;
+  const unsigned extent = w1 > w0 ? (unsigned)(w1 - w0 - 1) * stride_b + D * 2 : 0u;
   const __amdgpu_buffer_rsrc_t rs_k = make_rsrc(p.k + head_off, extent);
   const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(p.v + head_off, extent);
   char* wl = smem + wave * 2 * STAGE;       // this wave's two V stages
@@ -100,11 +102,11 @@ void decode_partial_kernel(DecodeParams p, int g) {
   auto issue_k = [&](int k0, int slot) {
 #pragma unroll
     for (int s = 0; s < DS; ++s)
-      kr[slot][s] = __builtin_amdgcn_raw_buffer_load_b128(rs_k, (int)((unsigned)k0 * stride_b + koff + 32u * s), 0, 0);
+      kr[slot][s] = __builtin_amdgcn_raw_buffer_load_b128(rs_k, (int)((unsigned)(k0 - w0) * stride_b + koff + 32u * s), 0, 0);
   };
   auto issue_v = [&](int k0, int stage) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) dma16(rs_v, (unsigned)k0 * stride_b + voff_v[i], wl + stage * STAGE + 1024 * i);
+    for (int i = 0; i < NV; ++i) dma16(rs_v, (unsigned)(k0 - w0) * stride_b + voff_v[i], wl + stage * STAGE + 1024 * i);
   };
 
   f32x16 oacc[DB];
@@ -178,9 +180,9 @@ void decode_partial_kernel(DecodeParams p, int g) {
 
   // Step st uses K buffer st % NKB and V stage st % 2.  Loads of step st + 2
   // (st + 1 with one K buffer) are issued as soon as their buffer is free.
-  // The loads are issued unconditionally -- past the wave's range they hit
-  // offsets beyond the resource (read as zero) or other waves' keys, and are
-  // never used -- so every step sees the same number of younger loads in
+  // The loads are issued unconditionally -- past the unit's keys they hit
+  // offsets beyond the resource, read as zero without a memory access, and
+  // are never used -- so every step sees the same number of younger loads in
   // flight and the waits below are exact.
   issue_k(w0, 0);
   issue_v(w0, 0);
