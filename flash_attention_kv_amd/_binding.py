@@ -86,6 +86,17 @@ def _dev(*ts: torch.Tensor):
     return dev
 
 
+def _out_like(out: Optional[torch.Tensor], ref: torch.Tensor) -> torch.Tensor:
+    """The caller's output tensor, checked to be exactly like ref (device,
+    dtype, shape, contiguity), or a new one."""
+    if out is None:
+        return torch.empty_like(ref)
+    _dev(ref, out)
+    if out.dtype != ref.dtype or out.shape != ref.shape:
+        raise ValueError(f"out must be {ref.dtype} {tuple(ref.shape)}, got {out.dtype} {tuple(out.shape)}")
+    return out
+
+
 def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -133,7 +144,7 @@ def ring_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, C: int =
         if Tt % n_seqs or St % n_seqs:
             raise ValueError("token counts must divide by n_seqs")
         T_q, S_kv = Tt // n_seqs, St // n_seqs
-    o = out if out is not None else torch.empty_like(q)
+    o = _out_like(out, q)
     need = ring_attn_workspace_bytes(T_q, S_kv, h_q, h_kv, d, C, causal, n_seqs,
                                      seq_offsets is not None, dt)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
@@ -204,7 +215,7 @@ def splitkv_decode(q, k, v, *, n_chunks: int, workspace: Optional[torch.Tensor] 
     Bk, S, h_kv, dk = k.shape
     if Bk != B or dk != d or v.shape != k.shape:
         raise ValueError("shape mismatch between q, k and v")
-    o = out if out is not None else torch.empty_like(q)
+    o = _out_like(out, q)
     need = splitkv_decode_workspace_bytes(B, h_q, d, n_chunks)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)

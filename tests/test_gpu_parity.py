@@ -279,3 +279,18 @@ def test_jagged_bad_offsets_leave_output_untouched(dtype, offs):
                     seq_offsets=torch.tensor(offs, dtype=torch.int32, device=DEV), out=o)
     torch.cuda.synchronize()
     assert bool((o == 7.0).all())
+
+
+def test_binding_refuses_mismatched_out():
+    """A caller-supplied output must match q exactly; the binding refuses it
+    before anything is enqueued."""
+    q, k, v = (t.to(DEV) for t in _qkv(64, 64, 4, 2, 128, "bf16", 1))
+    for bad in (torch.empty(63, 4, 128, dtype=torch.bfloat16, device=DEV),
+                torch.empty(64, 4, 128, dtype=torch.float32, device=DEV),
+                torch.empty(4, 64, 128, dtype=torch.bfloat16, device=DEV).transpose(0, 1)):
+        with pytest.raises(ValueError):
+            F.ring_attn_fwd(q, k, v, causal=True, out=bad)
+    qd = q[:2].clone()                                    # decode: (B=2, h_q=4, d)
+    kc = torch.zeros(2, 64, 2, 128, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        F.splitkv_decode(qd, kc, kc, n_chunks=2, out=torch.empty(2, 4, 64, dtype=torch.bfloat16, device=DEV))
