@@ -149,6 +149,8 @@ def ring_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, C: int =
                                      seq_offsets is not None, dt)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif need:
+        _dev(q, workspace)
     if window is None:
         st = lib().ring_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), T_q, S_kv, h_q, h_kv, d, C,
                                  int(causal), _ptr(seq_offsets), n_seqs, dt,
@@ -219,6 +221,8 @@ def splitkv_decode(q, k, v, *, n_chunks: int, workspace: Optional[torch.Tensor] 
     need = splitkv_decode_workspace_bytes(B, h_q, d, n_chunks)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    else:
+        _dev(q, workspace)
     st = lib().splitkv_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, h_q, h_kv, d, S, n_chunks, dt,
                               _ptr(workspace), need, _stream(dev))
     _check("splitkv_decode", st)

@@ -294,3 +294,6 @@ def test_binding_refuses_mismatched_out():
     kc = torch.zeros(2, 64, 2, 128, dtype=torch.bfloat16, device=DEV)
     with pytest.raises(ValueError):
         F.splitkv_decode(qd, kc, kc, n_chunks=2, out=torch.empty(2, 4, 64, dtype=torch.bfloat16, device=DEV))
+    ws = F.splitkv_decode_workspace_bytes(2, 4, 128, 2)
+    with pytest.raises(ValueError):                       # a workspace must be on the same device
+        F.splitkv_decode(qd, kc, kc, n_chunks=2, workspace=torch.empty(ws, dtype=torch.uint8))
