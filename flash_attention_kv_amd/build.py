@@ -22,6 +22,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfakv.so")
+EXAMPLE = os.path.join(PKG, "examples", "abi_consumer")
 ARCH = os.environ.get("FAKV_OFFLOAD_ARCH", "gfx950")
 
 
@@ -58,8 +59,16 @@ def build(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    # the plain-C consumer of the ABI (no Python), linked against the library
+    rocm = os.path.dirname(os.path.dirname(hipcc()))
+    cmd = [hipcc(), "-O2", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(rocm, "include"),
+           "-I", os.path.join(ROOT, "include"), "-o", EXAMPLE,
+           os.path.join(PKG, "examples", "abi_consumer.c"), "-L", PKG, "-lfakv", "-Wl,-rpath,$ORIGIN/.."]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"abi_consumer build failed:\n{r.stderr}")
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources", file=sys.stderr)
+        print(f"built {LIB} from {len(srcs)} sources, and {EXAMPLE}", file=sys.stderr)
     return LIB
 
 
