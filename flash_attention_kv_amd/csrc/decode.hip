@@ -13,9 +13,10 @@
 // in steps of 32 keys, two steps in flight, with no barrier anywhere:
 //   K: each lane loads its key row's dims straight into the MFMA A operand of
 //      S^T = K Q^T (key rows are how K is stored), double-buffered registers;
-//   V: 32 x d tiles go HBM -> LDS directly (buffer_load ... lds) into two
-//      wave-private stages, swizzled so that the A operand of O^T += V^T P^T
-//      is read with the conflict-free transpose read ds_read_b64_tr_b16.
+//   V: 32 x d tiles go HBM -> LDS directly (buffer_load ... lds, with the
+//      non-temporal hint: every byte is read once) into two wave-private
+//      stages, swizzled so that the A operand of O^T += V^T P^T is read with
+//      the conflict-free transpose read ds_read_b64_tr_b16.
 // Buffer resources span one unit's keys (one chunk of one sequence and KV
 // head), so no load can leave the unit.  Each wave writes its unit's triplet: m, l
 // (n_chunks, B*h_q) and O unnormalised (n_chunks, B*h_q, d), the layout
@@ -106,7 +107,7 @@ void decode_partial_kernel(DecodeParams p, int g) {
   };
   auto issue_v = [&](int k0, int stage) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) dma16(rs_v, (unsigned)(k0 - w0) * stride_b + voff_v[i], wl + stage * STAGE + 1024 * i);
+    for (int i = 0; i < NV; ++i) dma16_stream(rs_v, (unsigned)(k0 - w0) * stride_b + voff_v[i], wl + stage * STAGE + 1024 * i);
   };
 
   f32x16 oacc[DB];
