@@ -13,7 +13,10 @@ and the 4-chunk fp32 ring latency case.
 
 Timing: W untimed warm-up steps, then K steps, each bracketed by HIP events
 recorded on the stream the library launches on (torch's current stream); the
-timed region is bracketed by device synchronisation.  `roofline.achieved` is
+timed region is bracketed by device synchronisation.  The default W is 30:
+after idle the GPU runs its first ~20 launches of the headline workload about
+15 % slower (0.60 against 0.52 ms) before it settles, so a short warm-up
+measures that ramp rather than the kernel.  `roofline.achieved` is
 the dominant kernel's algorithmic work per launch over its average event-timed
 duration.  `roofline.traffic` comes from the committed rocprofv3 counter
 summary when it was taken on the current kernel sources, else null.
@@ -181,7 +184,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workloads", default="gqa_ring,dense_causal,jagged,gqa_swa,decode,ring_tiny")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
