@@ -85,9 +85,11 @@ JaggedLayout jagged_layout(int T_q, int n_seqs, int BQ, int n_hg, bool sched) {
   return L;
 }
 
+// empty: the call has no query rows, so no tensor is read and null pointers
+// are accepted.
 fakv_status check_prefill_common(const void* q, const void* k, const void* v, int h_q, int h_kv,
-                                 int d, int dtype) {
-  if (!q || !k || !v) return fail(FAKV_EINVAL, "q, k and v must be non-null");
+                                 int d, int dtype, bool empty = false) {
+  if ((!q || !k || !v) && !empty) return fail(FAKV_EINVAL, "q, k and v must be non-null");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v))
     return fail(FAKV_EINVAL, "q, k and v must be 16-byte aligned");
   if (h_q < 1 || h_kv < 1) return fail(FAKV_EINVAL, "h_q and h_kv must be >= 1 (got %d, %d)", h_q, h_kv);
@@ -151,9 +153,9 @@ static fakv_status ring_attn_impl(const void* q, const void* k, const void* v, v
                                   int h_q, int h_kv, int d, int C, int causal, int window,
                                   const int32_t* seq_offsets, int n_seqs, int dtype, void* workspace,
                                   size_t workspace_bytes, void* stream) {
-  fakv_status s = check_prefill_common(q, k, v, h_q, h_kv, d, dtype);
+  fakv_status s = check_prefill_common(q, k, v, h_q, h_kv, d, dtype, T_q == 0);
   if (s != FAKV_OK) return s;
-  if (!o) return fail(FAKV_EINVAL, "o must be non-null");
+  if (!o && T_q != 0) return fail(FAKV_EINVAL, "o must be non-null");
   if (!aligned16(o)) return fail(FAKV_EINVAL, "o must be 16-byte aligned");
   if (T_q < 0 || S_kv < 0) return fail(FAKV_EINVAL, "T_q and S_kv must be >= 0");
   if (C < 1) return fail(FAKV_EINVAL, "C must be >= 1 (got %d)", C);
@@ -192,6 +194,7 @@ static fakv_status ring_attn_impl(const void* q, const void* k, const void* v, v
     return fail(FAKV_EINVAL, "seq_offsets must be 4-byte aligned");
   if ((long long)T_q * h_q * d >= (1ll << 40)) return fail(FAKV_EINVAL, "tensor too large");
   if ((s = check_kv_extent(S_kv, h_kv, d, dtype)) != FAKV_OK) return s;
+  if (T_q == 0) return FAKV_OK;              // every sequence empty: no workspace, nothing to do
   const size_t need = ring_attn_workspace_bytes(T_q, S_kv, h_q, h_kv, d, C, causal, n_seqs, 1, dtype);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(FAKV_EINVAL, "workspace too small: need %zu bytes, got %zu", need, workspace_bytes);
@@ -261,9 +264,9 @@ fakv_status attn_partial(const void* q, const void* k, const void* v, float* m, 
                          float* o_acc, int T_q, int S_chunk, int h_q, int h_kv, int d, int q_pos0,
                          int k_pos0, int causal, int accumulate, int dtype, void* stream) {
   g_err.clear();
-  fakv_status s = check_prefill_common(q, k, v, h_q, h_kv, d, dtype);
+  fakv_status s = check_prefill_common(q, k, v, h_q, h_kv, d, dtype, T_q == 0);
   if (s != FAKV_OK) return s;
-  if (!m || !l || !o_acc) return fail(FAKV_EINVAL, "m, l and o_acc must be non-null");
+  if ((!m || !l || !o_acc) && T_q != 0) return fail(FAKV_EINVAL, "m, l and o_acc must be non-null");
   if (!aligned16(o_acc) || !aligned16(m) || !aligned16(l))
     return fail(FAKV_EINVAL, "m, l and o_acc must be 16-byte aligned");
   if (T_q < 0 || S_chunk < 0) return fail(FAKV_EINVAL, "T_q and S_chunk must be >= 0");

@@ -79,7 +79,8 @@ typedef enum { FAKV_F32 = 0, FAKV_BF16 = 1 } fakv_dtype;
  *                    online-softmax step); a row with no admissible key keeps
  *                    its state.
  * Preconditions: T_q >= 0, S_chunk >= 0, h_q % h_kv == 0.  T_q == 0 enqueues
- * nothing; S_chunk == 0 writes identities (accumulate == 0) or nothing.
+ * nothing (the pointers may then be NULL); S_chunk == 0 writes identities
+ * (accumulate == 0) or nothing.
  */
 fakv_status attn_partial(const void* q, const void* k, const void* v,
                          float* m, float* l, float* o_acc,
@@ -128,7 +129,9 @@ fakv_status lse_merge(const float* m_parts, const float* l_parts, const float* o
  * ends at min(chunk end, query tile end) ("dependent Tile.end"), so only the
  * tiles straddling the diagonal apply an element mask.
  * workspace: at least ring_attn_workspace_bytes(...) bytes (may be NULL when
- * that is 0).
+ * that is 0).  T_q == 0 (an empty dense batch, or a jagged batch whose
+ * sequences are all empty) is a valid call that enqueues nothing; q, k, v, o
+ * and workspace may then be NULL.
  */
 fakv_status ring_attn_fwd(const void* q, const void* k, const void* v, void* o,
                           int T_q, int S_kv, int h_q, int h_kv, int d, int C, int causal,

@@ -85,6 +85,15 @@ def test_ring_attn_fwd_rejects(kw, code, msg):
 def test_valid_empty_call_enqueues_nothing():
     # T_q == 0 is valid and returns before any HIP call
     assert _ring(T_q=0, S_kv=0) == 0 and F.lib().fakv_last_error() == b""
+    # nothing is read or written, so the data pointers may be NULL
+    assert _ring(q=None, k=None, v=None, o=None, T_q=0, S_kv=0) == 0
+    # a jagged batch of empty sequences: the workspace size is 0 and none is needed
+    assert F.ring_attn_workspace_bytes(0, 0, 4, 2, 128, 1, 1, 3, 1, F.BF16) == 0
+    assert _ring(q=None, k=None, v=None, o=None, T_q=0, S_kv=0, seq_offsets=16, n_seqs=3) == 0
+    assert F.lib().attn_partial(None, None, None, None, None, None, 0, 64, 4, 2, 128, 0, 0, 1, 1,
+                                F.BF16, None) == 0
+    # with rows to compute, NULL data pointers are still refused
+    assert _ring(q=None, T_q=8, S_kv=8) == EINVAL
 
 
 def test_other_entry_points_reject():
