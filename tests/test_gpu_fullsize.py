@@ -85,3 +85,65 @@ def test_decode_fullsize_sampled():
         got.append(o[b, h].float().numpy().astype(np.float64))
         ref.append(oracle.attention_rows_ref(qc[b:b + 1], kc[b], vc[b], [0], [h])[0])
     check(np.array(got), np.array(ref), "bf16", "decode sampled rows")
+
+
+def _ring_chunks(w):
+    q, k, v, _ = make_prefill_inputs(w, device=DEV)
+    n = w.S_kv // w.C
+    qs = [q[r * n:(r + 1) * n] for r in range(w.C)]
+    ks = [k[c * n:(c + 1) * n] for c in range(w.C)]
+    vs = [v[c * n:(c + 1) * n] for c in range(w.C)]
+    return q, k, v, qs, ks, vs, n
+
+
+def test_ring_from_chunk_partials_fullsize_sampled():
+    """The GQA ring at full size assembled from the chunk-level entry point,
+    as the prefill page's ranks run it: rank r folds chunk (r + s) mod C into
+    its running (m, l, O) at step s (attn_partial with accumulate), then
+    divides by l.  Chunks wholly after the rank's queries are still passed and
+    must leave the state unchanged."""
+    w = WORKLOADS["gqa_ring"]
+    q, k, v, qs, ks, vs, n = _ring_chunks(w)
+    outs = []
+    for r in range(w.C):
+        state = None
+        for s in range(w.C):
+            c = (r + s) % w.C
+            state = F.attn_partial(qs[r], ks[c], vs[c], q_pos0=r * n, k_pos0=c * n, causal=True, state=state)
+        m, l, o = state
+        outs.append((o / l.unsqueeze(-1)).cpu())
+    torch.cuda.synchronize()
+    got_all = torch.cat(outs)
+    assert torch.isfinite(got_all).all()
+    rng = np.random.default_rng(11)
+    toks, heads = _sample_rows(w.T_q, w.h_q, rng, extra=[c * n + e for c in range(w.C) for e in (-1, 0)])
+    ref = oracle.attention_rows_ref(q.cpu(), k.cpu(), v.cpu(), toks, heads, causal=True)
+    check(got_all.numpy()[toks, heads].astype(np.float64), ref, "bf16", "ring from attn_partial", out_bf16=False)
+
+
+def test_lse_merge_of_chunk_partials_fullsize_sampled():
+    """The same ring as C separate chunk partials per rank (accumulate = 0)
+    folded by one n-way lse_merge, rows = tokens x heads: parts of chunks
+    after a rank's queries are empty (m = -inf, l = 0) and must weigh 0."""
+    w = WORKLOADS["gqa_ring"]
+    q, k, v, qs, ks, vs, n = _ring_chunks(w)
+    rows = w.T_q * w.h_q
+    m_parts = torch.empty(w.C, rows, dtype=torch.float32, device=DEV)
+    l_parts = torch.empty_like(m_parts)
+    o_parts = torch.empty(w.C, rows, w.d, dtype=torch.float32, device=DEV)
+    for r in range(w.C):
+        sl = slice(r * n * w.h_q, (r + 1) * n * w.h_q)
+        for s in range(w.C):
+            c = (r + s) % w.C
+            m, l, o = F.attn_partial(qs[r], ks[c], vs[c], q_pos0=r * n, k_pos0=c * n, causal=True)
+            m_parts[s, sl] = m.reshape(-1)
+            l_parts[s, sl] = l.reshape(-1)
+            o_parts[s, sl] = o.reshape(-1, w.d)
+    out, lse = F.lse_merge(m_parts, l_parts, o_parts, out_dtype=torch.bfloat16, return_lse=True)
+    torch.cuda.synchronize()
+    out = out.reshape(w.T_q, w.h_q, w.d).cpu()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    rng = np.random.default_rng(12)
+    toks, heads = _sample_rows(w.T_q, w.h_q, rng, extra=[c * n + e for c in range(w.C) for e in (-1, 0)])
+    ref = oracle.attention_rows_ref(q.cpu(), k.cpu(), v.cpu(), toks, heads, causal=True)
+    check(out.float().numpy()[toks, heads].astype(np.float64), ref, "bf16", "lse_merge of chunk partials")
