@@ -14,9 +14,10 @@
 //   1. K and V tiles go HBM -> LDS directly (buffer_load_dwordx4 ... lds: no
 //      register staging), double-buffered: tile t+1 is in flight while tile t
 //      computes.  Keys past the tile's valid end are masked.
-//   2. S^T = K Q^T on MFMA (Q resident in registers as the B operand); for
-//      d <= 128 the LDS operand reads are inline asm with explicit lgkmcnt
-//      waits so that the prefetch of tile t+1 is not waited for early.
+//   2. S^T = K Q^T on MFMA (Q resident in registers as the B operand).  The
+//      LDS operand reads are inline asm with explicit lgkmcnt waits, one
+//      k-step ahead of the MFMAs, so that the prefetch of tile t+1 is not
+//      waited for early and no read waits for the one before it.
 //   3. The online-softmax fold of the prefill page's ring step, with the
 //      block partial folded directly into the running (m, l, O): row max,
 //      exp2 of pre-scaled scores, per-lane partial row sums.  l and O are
@@ -48,9 +49,6 @@ __device__ __forceinline__ void wait_dma_and_sync() {
   __syncthreads();
 }
 
-__device__ __forceinline__ bf16x4 tr16(const char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 __attribute__((address_space(3)))*)(p));
-}
 
 // Geometry of one work item: a query tile [q_lo, q_hi) of one sequence
 // (local indices) and one head group, against that sequence's keys.
@@ -216,9 +214,6 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
 
     const bool skip = !wave_active || (p.causal && p.prune && kt > qw_hi - 1 + delta) ||
                       (win > 0 && p.prune && kt + BK - 1 < qw_lo + delta - win + 1);
-    // (d = 256 keeps the builtin reads: the extra staging registers of the
-    // asm path push it into spills.)
-    if constexpr (D <= 128) {
     if (!skip) {
       // Every LDS read below is inline asm with explicit lgkmcnt waits: the
       // compiler would otherwise wait for the next tile's HBM -> LDS loads
@@ -256,8 +251,9 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
       });
       // V^T reads go in groups of VG dim blocks (2 VG reads, within the
       // lgkmcnt range), one group ahead of the MFMAs; the first group is in
-      // flight while the softmax runs.
-      constexpr int VG = DB < 4 ? DB : 4;
+      // flight while the softmax runs.  VG is 2 at d = 256, whose O and Q
+      // leave few registers for staging.
+      constexpr int VG = DB < 4 ? DB : (D == 256 ? 2 : 4);
       constexpr int NG = DB / VG;
       u32x2 va[2][VG][2];
       auto issue_v = [&](auto ic, auto slotc) {
@@ -338,83 +334,6 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
           oacc[g0 + b] = mfma32x32x16(__builtin_bit_cast(bf16x8, a4), pb[ks], oacc[g0 + b]);
         });
       });
-    }
-    } else {
-    if (!skip) {
-      const char* kl = smem + BUF * 2 * TILE;
-      const char* vl = kl + TILE;
-      // S^T = K Q^T
-      f32x16 sacc[KB];
-#pragma unroll
-      for (int b = 0; b < KB; ++b) sacc[b] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < DS; ++s) {
-#pragma unroll
-        for (int b = 0; b < KB; ++b) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl + koff[s % 8] + (s / 8) * 256 + b * 32 * (D * 2));
-          sacc[b] = mfma32x32x16(a, qreg[s], sacc[b]);
-        }
-      }
-      // element mask only on tiles that cross the tail or the diagonal
-      const bool need_mask = (kt + BK > end) || (p.causal && (kt + BK - 1 > qw_lo + delta)) ||
-                             (win > 0 && kt < qw_hi - 1 + delta - win + 1);
-      if (need_mask) {
-        const int qlim = qi + delta;
-#pragma unroll
-        for (int b = 0; b < KB; ++b)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kt + 32 * b + 8 * (r >> 2) + 4 * half + (r & 3);
-            const bool ok = key < end && (!p.causal || key <= qlim) && (win == 0 || key > qlim - win);
-            if (!ok) sacc[b][r] = neg_inf();
-          }
-      }
-      // online softmax fold
-      float mt = neg_inf();
-#pragma unroll
-      for (int b = 0; b < KB; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[b][r]);
-      mt = halves_max(mt);
-      m_true = fmaxf(m_true, mt * scale);
-      if (__builtin_amdgcn_ballot_w64(m_true > m_sh + kLazyShift * kLn2) != 0) {
-        // move the shift to the true max: rescale by exp(m_sh - m_true)
-        // (0 for an empty state)
-        const float mu = (m_true == neg_inf()) ? 0.f : m_true;
-        const float alpha = fast_exp2((m_sh - mu) * kLog2e);
-        m_sh = m_true;
-        l_run *= alpha;
-#pragma unroll
-        for (int b = 0; b < DB; ++b)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
-      }
-      const float mlog = ((m_sh == neg_inf()) ? 0.f : m_sh) * kLog2e;
-#pragma unroll
-      for (int b = 0; b < KB; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(__builtin_fmaf(sacc[b][r], scale_log2, -mlog));
-          sacc[b][r] = e;
-          l_run += e;
-        }
-      // O^T += V^T P^T
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        float pv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pv[j] = sacc[ks >> 1][8 * (ks & 1) + j];
-        const bf16x8 pb = pack_bf16x8(pv);
-#pragma unroll
-        for (int b = 0; b < DB; ++b) {
-          const char* a1 = vl + voff[b % 4] + (b / 4) * 256 + 16 * ks * (D * 2);
-          const bf16x4 lo = tr16(a1);
-          const bf16x4 hi = tr16(a1 + 8 * (D * 2));
-          const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[b] = mfma32x32x16(a, pb, oacc[b]);
-        }
-      }
-    }
     }
     wait_dma_and_sync();
     walk = nxt;
