@@ -272,14 +272,23 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
       const bool need_mask = (kt + BK > end) || (p.causal && (kt + BK - 1 > qw_lo + delta)) ||
                              (win > 0 && kt < qw_hi - 1 + delta - win + 1);
       if (need_mask) {
+        // Key kt + 4 half + j of register r of block b (j = 32 b + 8 (r / 4)
+        // + r % 4, a constant) is admissible for the lane's row iff
+        // lo < j < hi: the tail, causal and window bounds folded into two
+        // per-lane limits, so each score costs one compare of j - (lo + 1)
+        // against hi - lo - 1 (unsigned) and a select.
         const int qlim = qi + delta;
+        const int k0 = kt + 4 * half;
+        const int hi = p.causal ? min(end, qlim + 1) - k0 : end - k0;
+        const int lo = win > 0 ? qlim - win - k0 : -1;
+        const unsigned first = (unsigned)(lo + 1);
+        const unsigned span = hi > lo + 1 ? (unsigned)(hi - lo - 1) : 0u;
 #pragma unroll
         for (int b = 0; b < KB; ++b)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = kt + 32 * b + 8 * (r >> 2) + 4 * half + (r & 3);
-            const bool ok = key < end && (!p.causal || key <= qlim) && (win == 0 || key > qlim - win);
-            if (!ok) sacc[b][r] = neg_inf();
+            const unsigned j = 32 * b + 8 * (r >> 2) + (r & 3);
+            sacc[b][r] = j - first < span ? sacc[b][r] : neg_inf();
           }
       }
       float mt = neg_inf();
