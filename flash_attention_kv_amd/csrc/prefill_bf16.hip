@@ -402,41 +402,56 @@ void prefill_bf16_kernel(PrefillParams p) {
     // so the query tiles that share one sequence's K/V run on one XCD and
     // hit its L2.  The grid is a multiple of 8; the G / 8 workgroups of XCD x
     // deal the entries of queue x among themselves in zigzag rounds.  No
-    // atomics: every workgroup knows its entries,
-    // so the next entry and its item record are fetched while the current
-    // item computes.
+    // atomics: every workgroup knows its entries.  The next item's record
+    // and the entry after it come in with one vector load issued before the
+    // current item runs -- lanes 0..3 fetch record words 2, 3, 4 and 6, lane
+    // 4 the queue entry, so the value is not uniform and stays in a vector
+    // register until it is read after the item: the chain entry -> record
+    // never stalls an item's start.
     const int x = blockIdx.x & 7;
     const int nj = gridDim.x >> 3;
     const int len = p.qinfo[x];
-    const int* q = p.sched + (size_t)x * p.sched_stride;
-    auto load = [&](int slot, ItemGeo& g) -> bool {
-      if (slot >= len) return false;
-      const int e = q[slot];
-      const int item = e / p.n_hg;
-      const int32_t* it = p.items + 8 * (size_t)item;
-      g.seq_q0 = g.seq_k0 = it[2];
-      g.Lq = g.Lk = it[3];
-      g.q_lo = it[4] - it[2];
-      g.q_hi = it[6] - it[2];
-      g.hg = e - item * p.n_hg;
-      g.jagged = 1;
-      return true;
-    };
+    const int32_t* q = p.sched + (size_t)x * p.sched_stride;
+    const int lane = threadIdx.x & 63;
     // Round r covers slots [r nj, (r + 1) nj); workgroup j takes slot j of
     // even rounds and slot nj - 1 - j of odd ones, so a workgroup that drew a
     // long tile of a unit draws a short one next.
     const int j = blockIdx.x >> 3;
     auto slot_of = [&](int r) { return r * nj + ((r & 1) ? nj - 1 - j : j); };
-    int r = 0;
-    ItemGeo g;
-    bool have = load(slot_of(0), g);
-    while (have) {
-      ItemGeo gn;
-      const bool have_n = load(slot_of(r + 1), gn);
+    // record of the item of entry e (item 0 when e < 0, read and ignored) and
+    // the entry at slot (entry 0 when slot >= len, read and ignored)
+    auto fetch = [&](int e, int slot) {
+      const int32_t* it = p.items + 8 * (size_t)(e >= 0 ? e / p.n_hg : 0);
+      const int li = lane & 7;
+      const int32_t* a = li == 0 ? it + 2 : li == 1 ? it + 3 : li == 2 ? it + 4 : li == 3 ? it + 6
+                                                                        : q + (slot < len ? slot : 0);
+      return *a;
+    };
+    struct Rec { int s0, L, lo, hi; };
+    auto rec_of = [&](int v) {
+      return Rec{__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 1),
+                 __builtin_amdgcn_readlane(v, 2), __builtin_amdgcn_readlane(v, 3)};
+    };
+    auto entry_of = [&](int v, int slot) { return slot < len ? __builtin_amdgcn_readlane(v, 4) : -1; };
+    if (slot_of(0) >= len) return;
+    int e0 = q[slot_of(0)];
+    const int v0 = fetch(e0, slot_of(1));
+    Rec rc = rec_of(v0);
+    int e1 = entry_of(v0, slot_of(1));
+    for (int r = 0;; ++r) {
+      const int vn = fetch(e1, slot_of(r + 2));   // record of item r + 1, entry of item r + 2
+      ItemGeo g;
+      g.seq_q0 = g.seq_k0 = rc.s0;
+      g.Lq = g.Lk = rc.L;
+      g.q_lo = rc.lo - rc.s0;
+      g.q_hi = rc.hi - rc.s0;
+      g.hg = e0 % p.n_hg;
+      g.jagged = 1;
       prefill_item<D, QH, NW>(p, smem, g);
-      ++r;
-      g = gn;
-      have = have_n;
+      if (e1 < 0) break;
+      rc = rec_of(vn);
+      e0 = e1;
+      e1 = entry_of(vn, slot_of(r + 2));
     }
     return;
   }
