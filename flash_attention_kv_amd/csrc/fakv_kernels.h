@@ -64,6 +64,9 @@ hipError_t ensure_lds_limit(const void* fn, int bytes, std::atomic<unsigned>& do
 // per workgroup, for a dense or a jagged batch.
 int prefill_bf16_query_rows(int d, int qh, bool jagged);
 hipError_t launch_prefill_bf16(const PrefillParams& p, int d, int qh, int grid, hipStream_t stream);
+// d = 256 instances (their own translation unit, see prefill_bf16_d256.hip)
+hipError_t launch_prefill_bf16_d256(const PrefillParams& p, int qh, int grid, hipStream_t stream);
+int prefill_bf16_resident_d256(int qh);
 hipError_t launch_prefill_f32(const PrefillParams& p, int d, int grid, hipStream_t stream);
 constexpr int kF32QueryTile = 128;   // query rows per fp32 workgroup
 hipError_t launch_decode_partial(const DecodeParams& p, int d, int g, hipStream_t stream);
