@@ -11,17 +11,26 @@ d = 256 workload, the jagged 1152-sequence workload, the split-KV decode
 workload (HBM GB/s), the GQA ring shape with a 2048-key causal sliding window
 and the 4-chunk fp32 ring latency case.
 
-Timing: W untimed warm-up steps, then K steps, each bracketed by HIP events
-recorded on the stream the library launches on (torch's current stream); the
-timed region is bracketed by device synchronisation.  The default W is 30:
-after idle the GPU runs its first ~20 launches of the headline workload about
-15 % slower (0.60 against 0.52 ms) before it settles, so a short warm-up
-measures that ramp rather than the kernel.  `roofline.achieved` is
-the dominant kernel's algorithmic work per launch over its average event-timed
-duration.  `roofline.traffic` comes from the committed rocprofv3 counter
-summary when it was taken on the current kernel sources, else null.
-`cpu_baseline` times the fp64 NumPy oracle as it stands on a bounded sample of
-the headline workload (whole query heads, all rows), on this host's cores.
+Per workload:
+  1. settle: the step runs back to back for --settle seconds, which brings the
+     GPU from idle to its loaded clock before anything is timed.
+  2. W untimed warm-up steps, then K steps, each bracketed by HIP events
+     recorded on the stream the library launches on (torch's current stream);
+     the timed region is bracketed by device synchronisation.  ms_per_step is
+     the mean of the K event times, median_ms their median.
+`roofline.achieved` is the dominant kernel's algorithmic work per launch over
+that mean.  `roofline.traffic` (HBM bytes per launch) and
+`roofline.at_measured_clock` (the peak at the clock the counters measured
+under this load: CUs x clock x 4096 dense bf16 FLOP/clk/CU) come from the
+committed rocprofv3 counter summary when it was taken on the current kernel
+sources, else they are null.
+
+CPU leg (skipped with --no-cpu-baseline): the fp64 NumPy oracle, as it stands,
+times a bounded sample of every workload on this host's cores -- whole query
+heads of the headline (`cpu_baseline`), whole (sequence, head) blocks or rows
+of the others -- and the GPU output of the last timed step is compared with it
+on that sample (max |err|, max |err| beyond the bf16 output rounding,
+Frobenius-relative error).
 """
 from __future__ import annotations
 
@@ -29,15 +38,17 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, nameplate
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+BF16_FLOP_PER_CLK_CU = 4096    # dense bf16 MFMA FLOP per clock per CU
 METRIC = "useful causal TFLOP/s (prefill) and HBM GB/s (split-KV decode), % of roofline"
 
 
@@ -50,10 +61,11 @@ def csrc_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str):
-    """HBM bytes per launch from the committed counter summary, if it was
-    measured on the current kernel sources."""
-    p = os.path.join(ROOT, "profiles", "traffic.json")
+def load_counter(workload: str, key: str):
+    """A per-launch figure of the dominant kernel from the committed rocprofv3
+    counter summary (profiles/counters.json), if it was measured on the
+    current kernel sources, else None."""
+    p = os.path.join(ROOT, "profiles", "counters.json")
     if not os.path.exists(p):
         return None
     try:
@@ -63,7 +75,25 @@ def load_traffic(workload: str):
     ent = data.get(workload)
     if not ent or ent.get("csrc_hash") != csrc_hash():
         return None
-    return ent.get("bytes_per_launch")
+    return ent.get(key)
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel
+    calibration)."""
+    return load_counter(workload, "bytes_per_launch")
+
+
+def settle(fn, seconds: float):
+    """Runs fn back to back for `seconds`: from idle the GPU takes its first
+    ~20 launches of a sub-millisecond kernel to reach its loaded clock (they
+    run ~15 % slow), which a short warm-up would otherwise time."""
+    import torch
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
 
 
 def time_steps(fn, steps: int, warmup: int, stream):
@@ -80,11 +110,22 @@ def time_steps(fn, steps: int, warmup: int, stream):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per = [a.elapsed_time(b) for a, b in evs]
-    return sum(per) / len(per), wall
+    return sum(per) / len(per), statistics.median(per), wall
 
 
-def bench_prefill(name, steps, warmup, keep=False):
+def prefill_pairs(w, offs):
     import numpy as np
+    if offs is not None:
+        L = np.diff(offs.astype(np.int64))
+        return int((L * (L + 1) // 2).sum()) if w.causal else int((L * L).sum())
+    if w.window is not None:
+        # query i sees min(i + 1, W) keys
+        L, W = w.T_q, w.window
+        return w.n_seqs * (W * (W + 1) // 2 + max(0, L - W) * W if W < L else L * (L + 1) // 2)
+    return w.n_seqs * (w.T_q * (w.T_q + 1) // 2 if w.causal else w.T_q * w.S_kv)
+
+
+def bench_prefill(name, steps, warmup, settle_s):
     import torch
     import flash_attention_kv_amd as F
     from workloads import WORKLOADS, make_prefill_inputs
@@ -103,27 +144,18 @@ def bench_prefill(name, steps, warmup, keep=False):
         F.ring_attn_fwd(q, k, v, C=w.C, causal=w.causal, seq_offsets=offs_t, n_seqs=w.n_seqs,
                         workspace=ws, out=o, window=w.window)
 
-    ms, wall = time_steps(step, steps, warmup, stream)
-    if offs is not None:
-        L = np.diff(offs.astype(np.int64))
-        pairs = int((L * (L + 1) // 2).sum()) if w.causal else int((L * L).sum())
-    elif w.window is not None:
-        # query i sees min(i + 1, W) keys
-        L, W = w.T_q, w.window
-        pairs = w.n_seqs * (W * (W + 1) // 2 + max(0, L - W) * W if W < L else L * (L + 1) // 2)
-    else:
-        pairs = w.n_seqs * (w.T_q * (w.T_q + 1) // 2 if w.causal else w.T_q * w.S_kv)
-    flops = 4 * w.d * w.h_q * pairs
-    res = dict(ms=ms, wall_s=wall, flops=flops, tflops=flops / (ms * 1e-3) / 1e12, launches=1 if offs is None else 2)
-    if keep:
-        res["tensors"] = (q, k, v)
-    else:
-        del q, k, v, o, ws
-        torch.cuda.empty_cache()
+    settle(step, settle_s)
+    ms, med, wall = time_steps(step, steps, warmup, stream)
+    flops = 4 * w.d * w.h_q * prefill_pairs(w, offs)
+    res = dict(ms=ms, median_ms=med, wall_s=wall, flops=flops, tflops=flops / (ms * 1e-3) / 1e12)
+    # host copies for the CPU leg (inputs and the last step's output)
+    res["host"] = (q.cpu(), k.cpu(), v.cpu(), o.cpu(), offs)
+    del q, k, v, o, ws
+    torch.cuda.empty_cache()
     return res
 
 
-def bench_decode(steps, warmup):
+def bench_decode(steps, warmup, settle_s):
     import torch
     import flash_attention_kv_amd as F
     from workloads import WORKLOADS, make_decode_inputs
@@ -136,48 +168,124 @@ def bench_decode(steps, warmup):
     def step():
         F.splitkv_decode(q, k, v, n_chunks=w.n_chunks, workspace=ws, out=o)
 
-    ms, wall = time_steps(step, steps, warmup, stream)
+    settle(step, settle_s)
+    ms, med, wall = time_steps(step, steps, warmup, stream)
     kv_bytes = 2 * w.B * w.S_cache * w.h_kv * w.d * 2
     alg = kv_bytes + 2 * w.B * w.h_q * w.d * 2
     parts = 2 * w.n_chunks * w.B * w.h_q * (w.d + 2) * 4      # triplets written, then read
+    # host copies for the CPU leg: the rows of the first 2 sequences only
+    host = (q[:2].cpu(), k[:2].cpu(), v[:2].cpu(), o[:2].cpu())
     del q, k, v, o, ws
     torch.cuda.empty_cache()
-    return dict(ms=ms, wall_s=wall, bytes=alg, partial_bytes=parts, gbs=alg / (ms * 1e-3) / 1e9)
+    return dict(ms=ms, median_ms=med, wall_s=wall, bytes=alg, partial_bytes=parts,
+                gbs=alg / (ms * 1e-3) / 1e9, host=host)
 
 
-def cpu_baseline(tensors, budget_s: float = 12.0):
-    """Time the fp64 oracle on whole query heads of the headline workload."""
+# ---------------------------------------------------------------------------
+# CPU leg: the oracle on a bounded sample, timed, and the GPU output checked on it
+
+
+def _blas():
+    try:
+        from threadpoolctl import threadpool_info
+        return [(i.get("internal_api"), i.get("num_threads")) for i in threadpool_info()]
+    except Exception:   # pragma: no cover
+        return []
+
+
+class ErrAcc:
+    """Running parity statistics of GPU output blocks against the oracle."""
+
+    def __init__(self, out_bf16: bool):
+        self.out_bf16, self.mx, self.excess, self.se, self.sr = out_bf16, 0.0, 0.0, 0.0, 0.0
+
+    def add(self, got, ref):
+        import numpy as np
+        got = np.asarray(got, dtype=np.float64)
+        err = np.abs(got - ref)
+        if self.out_bf16:
+            # distance from ref to the set of values that round to the bf16 output
+            _, ex = np.frexp(got)
+            half_ulp = np.where(got == 0.0, 0.0, np.ldexp(1.0, ex - 9))
+            self.excess = max(self.excess, float((err - half_ulp).max()))
+        else:
+            self.excess = max(self.excess, float(err.max()))
+        self.mx = max(self.mx, float(err.max()))
+        self.se += float(np.square(got - ref).sum())
+        self.sr += float(np.square(ref).sum())
+
+    def report(self):
+        return {"max_abs": float(f"{self.mx:.4e}"), "max_abs_beyond_output_rounding": float(f"{self.excess:.4e}"),
+                "frob_rel": float(f"{(self.se / max(self.sr, 1e-300)) ** 0.5:.4e}")}
+
+
+def oracle_prefill_sample(name, host, budget_s: float):
+    """Whole (sequence, query head) blocks of a prefill workload, in a fixed
+    order, until `budget_s` of oracle time is used.  Returns the CPU rate and
+    the parity of the GPU output on those blocks."""
     import numpy as np
     import oracle
     from workloads import WORKLOADS
-    w = WORKLOADS["gqa_ring"]
-    q, k, v = tensors
-    g = w.h_q // w.h_kv
-    try:
-        from threadpoolctl import threadpool_info
-        blas = [(i.get("internal_api"), i.get("num_threads")) for i in threadpool_info()]
-    except Exception:   # pragma: no cover
-        blas = []
-    threads = max([n for _, n in blas if n] or [1])
-    done, t_used, flops = 0, 0.0, 0
-    t_start = time.perf_counter()
-    for h in range(w.h_q):
-        kvh = h // g
-        qh = q[:, h:h + 1].float().cpu().numpy()
-        kh = k[:, kvh:kvh + 1].float().cpu().numpy()
-        vh = v[:, kvh:kvh + 1].float().cpu().numpy()
+    w = WORKLOADS[name]
+    q, k, v, o, offs = host
+    if offs is not None:
+        segs = [(int(offs[b]), int(offs[b + 1])) for b in range(len(offs) - 1)]
+        order = [(b, h) for b in range(len(segs)) for h in range(w.h_q)]
+        keys = lambda b: segs[b]
+    else:
+        segs = [(b * w.T_q, (b + 1) * w.T_q) for b in range(w.n_seqs)]
+        # spread over sequences and heads: head h of sequence h mod n first
+        order = [((h + j) % w.n_seqs, h) for j in range(w.n_seqs) for h in range(w.h_q)]
+        keys = lambda b: (b * w.S_kv, (b + 1) * w.S_kv)
+    acc = ErrAcc(w.dtype == "bf16")
+    t_used, flops, blocks, rows = 0.0, 0, 0, 0
+    for (b, h) in order:
+        q0, q1 = segs[b]
+        k0, k1 = keys(b)
+        if q1 == q0:
+            continue
+        kvh = oracle.kv_head_of(h, w.h_q, w.h_kv)
+        qb, kb, vb = q[q0:q1, h:h + 1], k[k0:k1, kvh:kvh + 1], v[k0:k1, kvh:kvh + 1]
         t0 = time.perf_counter()
-        oracle.attention_ref(qh, kh, vh, causal=True)
+        ref = oracle.attention_ref(qb, kb, vb, causal=w.causal, window=w.window)
         t_used += time.perf_counter() - t0
-        done += 1
-        flops += 4 * w.d * (w.T_q * (w.T_q + 1) // 2)
+        acc.add(o[q0:q1, h].double().numpy(), ref[:, 0])
+        L, S = q1 - q0, k1 - k0
+        if w.window is not None:
+            pairs = oracle.windowed_pairs(L, w.window)
+        else:
+            pairs = oracle.causal_pairs(L) if w.causal else L * S
+        flops += oracle.useful_flops_prefill(1, w.d, pairs)
+        blocks += 1
+        rows += L
         if t_used >= budget_s:
             break
-    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {w.h_q} query heads of the GQA ring prefill workload (all {w.T_q} "
-                      f"causal query rows each), fp64 NumPy oracle, {t_used:.1f} s; BLAS {blas}; "
-                      f"host cpus {len(os.sched_getaffinity(0))}",
-            "seconds": round(t_used, 2)}
+    return {"tflops": flops / t_used / 1e12, "seconds": round(t_used, 2), "blocks": blocks, "rows": rows,
+            "of_blocks": sum(1 for (b, h) in order if segs[b][1] > segs[b][0]), "parity": acc.report()}
+
+
+def oracle_decode_sample(host, budget_s: float):
+    import oracle
+    from workloads import WORKLOADS
+    w = WORKLOADS["decode"]
+    q, k, v, o = host
+    acc = ErrAcc(True)
+    t_used, n, B = 0.0, 0, q.shape[0]
+    for b in range(B):
+        for h in range(w.h_q):
+            kvh = oracle.kv_head_of(h, w.h_q, w.h_kv)
+            t0 = time.perf_counter()
+            ref = oracle.attention_ref(q[b:b + 1, h:h + 1], k[b, :, kvh:kvh + 1], v[b, :, kvh:kvh + 1])
+            t_used += time.perf_counter() - t0
+            acc.add(o[b, h].double().numpy(), ref[0, 0])
+            n += 1
+            if t_used >= budget_s:
+                break
+        if t_used >= budget_s:
+            break
+    kv_bytes = 2 * w.S_cache * w.d * 2 * n / (w.h_q // w.h_kv)    # each KV head's cache serves g rows
+    return {"gbs": kv_bytes / t_used / 1e9, "seconds": round(t_used, 2), "rows": n,
+            "of_rows": w.B * w.h_q, "parity": acc.report()}
 
 
 def main():
@@ -185,6 +293,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--settle", type=float, default=0.5,
+                    help="seconds of back-to-back steps per workload before warm-up and timing")
     ap.add_argument("--workloads", default="gqa_ring,dense_causal,jagged,gqa_swa,decode,ring_tiny")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -209,60 +319,120 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copied_bytes": args.calibrate_copy}))
         return
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     sel = [s for s in args.workloads.split(",") if s]
-    extra = {}
-    head = None
-    if "gqa_ring" in sel:
-        head = bench_prefill("gqa_ring", args.steps, args.warmup, keep=not args.no_cpu_baseline)
-        print(f"# gqa_ring: {head['ms']:.3f} ms/step, {head['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
-    for name in ("dense_causal", "jagged", "gqa_swa"):
+    res = {}
+    for name in ("gqa_ring", "dense_causal", "jagged", "gqa_swa", "ring_tiny"):
         if name in sel:
-            r = bench_prefill(name, args.steps, args.warmup)
-            print(f"# {name}: {r['ms']:.3f} ms/step, {r['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+            r = bench_prefill(name, args.steps, args.warmup, args.settle)
+            res[name] = r
+            print(f"# {name}: {r['ms']:.4f} ms/step (median {r['median_ms']:.4f}), {r['tflops']:.1f} TFLOP/s",
+                  file=sys.stderr, flush=True)
+    if "decode" in sel:
+        r = bench_decode(args.steps, args.warmup, args.settle)
+        res["decode"] = r
+        print(f"# decode: {r['ms']:.4f} ms/step (median {r['median_ms']:.4f}), {r['gbs']:.0f} GB/s",
+              file=sys.stderr, flush=True)
+
+    def mfma_roofline(r, name):
+        out = {"bound": "mfma", "achieved": round(r["tflops"], 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+               "frac": round(r["tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": load_traffic(name)}
+        ghz = load_counter(name, "clock_ghz")
+        out["at_measured_clock"] = None
+        if ghz:
+            pk = n_cu * ghz * 1e9 * BF16_FLOP_PER_CLK_CU / 1e12
+            out["at_measured_clock"] = {"clock_ghz": ghz, "cus": n_cu, "peak": round(pk, 1),
+                                        "frac": round(r["tflops"] / pk, 4)}
+        return out
+
+    extra = {}
+    for name in ("dense_causal", "jagged", "gqa_swa"):
+        if name in res:
+            r = res[name]
             extra[name] = {"value": round(r["tflops"], 2), "unit": "TFLOP/s", "ms_per_step": round(r["ms"], 4),
-                           "useful_flops": r["flops"],
-                           "roofline": {"bound": "mfma", "achieved": round(r["tflops"], 2), "peak": PEAK_BF16_TFLOPS,
-                                        "unit": "TFLOP/s", "frac": round(r["tflops"] / PEAK_BF16_TFLOPS, 4),
-                                        "traffic": load_traffic(name)}}
+                           "median_ms": round(r["median_ms"], 4), "useful_flops": r["flops"],
+                           "roofline": mfma_roofline(r, name)}
     if "dense_causal" in extra:
         extra["dense_causal"]["page_context"] = "Pallas dense causal flash on the Helion page, same shape, unnamed chip: 225.8 TF/s"
     if "gqa_swa" in extra:
         extra["gqa_swa"]["window"] = 2048
     if "jagged" in extra:
         extra["jagged"]["page_context"] = "Helion page jagged table (softmax 'flash' row, unnamed chip, unknown lengths): 97.7 TF/s"
-    if "decode" in sel:
-        r = bench_decode(args.steps, args.warmup)
-        print(f"# decode: {r['ms']:.3f} ms/step, {r['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+    if "decode" in res:
+        r = res["decode"]
         extra["decode"] = {"value": round(r["gbs"], 1), "unit": "GB/s", "ms_per_step": round(r["ms"], 4),
+                           "median_ms": round(r["median_ms"], 4),
                            "algorithmic_bytes": r["bytes"], "partial_triplet_bytes": r["partial_bytes"],
                            "roofline": {"bound": "hbm", "achieved": round(r["gbs"], 1), "peak": PEAK_HBM_GBS,
                                         "unit": "GB/s", "frac": round(r["gbs"] / PEAK_HBM_GBS, 4),
                                         "traffic": load_traffic("decode")}}
-    if "ring_tiny" in sel:
-        r = bench_prefill("ring_tiny", args.steps, args.warmup)
+    if "ring_tiny" in res:
+        r = res["ring_tiny"]
         extra["ring_tiny"] = {"value": round(r["ms"] * 1e3, 2), "unit": "us per call", "dtype": "f32",
-                              "useful_flops": r["flops"]}
-    if head is None:
+                              "median_us": round(r["median_ms"] * 1e3, 2), "useful_flops": r["flops"],
+                              "tflops": round(r["tflops"], 3)}
+
+    # CPU leg: the oracle on a bounded sample of every workload
+    cpu = None
+    if not args.no_cpu_baseline:
+        blas = _blas()
+        threads = max([n for _, n in blas if n] or [1])
+        budgets = {"gqa_ring": 12.0, "dense_causal": 3.0, "jagged": 3.0, "gqa_swa": 3.0, "ring_tiny": 0.5}
+        for name, budget in budgets.items():
+            if name not in res:
+                continue
+            s = oracle_prefill_sample(name, res[name]["host"], budget)
+            print(f"# oracle {name}: {s['blocks']} blocks in {s['seconds']} s, parity {s['parity']}",
+                  file=sys.stderr, flush=True)
+            ent = {"seconds": s["seconds"], "value": round(s["tflops"], 4), "unit": "TFLOP/s", "cores": threads,
+                   "sample": f"{s['blocks']} of {s['of_blocks']} (sequence, query head) blocks, all rows "
+                             f"({s['rows']} rows), fp64 NumPy oracle"}
+            if name == "gqa_ring":
+                cpu = {"value": s["tflops"], "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                       "sample": f"{s['blocks']} of {w_heads(name)} query heads of the GQA ring prefill workload "
+                                 f"(all 8192 causal query rows each), fp64 NumPy oracle, {s['seconds']} s; "
+                                 f"BLAS {blas}; host cpus {len(os.sched_getaffinity(0))}",
+                       "seconds": s["seconds"], "parity": s["parity"]}
+            else:
+                extra[name]["oracle_cpu"] = ent
+                extra[name]["parity"] = s["parity"]
+        if "decode" in res:
+            s = oracle_decode_sample(res["decode"]["host"], 3.0)
+            print(f"# oracle decode: {s['rows']} rows in {s['seconds']} s, parity {s['parity']}",
+                  file=sys.stderr, flush=True)
+            extra["decode"]["oracle_cpu"] = {"seconds": s["seconds"], "value": round(s["gbs"], 3), "unit": "GB/s",
+                                             "cores": threads,
+                                             "sample": f"{s['rows']} of {s['of_rows']} (sequence, query head) "
+                                                       f"rows, fp64 NumPy oracle"}
+            extra["decode"]["parity"] = s["parity"]
+
+    if "gqa_ring" not in res:
         print(json.dumps({"metric": METRIC, "extra": extra}))
         return
-    cpu = None if args.no_cpu_baseline else cpu_baseline(head.pop("tensors"))
+    head = res["gqa_ring"]
+    roof = mfma_roofline(head, "gqa_ring")
+    roof["kernel"] = "prefill_bf16_kernel<128, 4, 4> (d=128, 4 query heads per 4-wave workgroup, 64-key tiles)"
+    roof["useful_flops_per_launch"] = head["flops"]
     line = {
         "metric": METRIC, "value": round(head["tflops"], 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["ms"], 4),
+        "median_ms": round(head["median_ms"], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic N(0,1), seeded, generated on the device",
         "config": {"workload": "gqa_ring_prefill", "h_q": 32, "h_kv": 8, "d_head": 128, "T_q": 8192,
                    "S_kv": 8192, "ring_chunks": 8, "causal": True, "global_batch": 1, "seq_len": 8192,
                    "parallelism": "1 GPU (ring ranks laid out on one device)"},
-        "roofline": {"bound": "mfma", "achieved": round(head["tflops"], 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(head["tflops"] / PEAK_BF16_TFLOPS, 4),
-                     "traffic": load_traffic("gqa_ring"),
-                     "kernel": "prefill_bf16_kernel<128, 4, 4> (d=128, 4 query heads per 4-wave workgroup, 64-key tiles)", "useful_flops_per_launch": head["flops"]},
+        "roofline": roof,
         "cpu_baseline": cpu,
         "extra": extra,
         "kernel_sources": csrc_hash(),
     }
     print(json.dumps(line), flush=True)
+
+
+def w_heads(name):
+    from workloads import WORKLOADS
+    return WORKLOADS[name].h_q
 
 
 if __name__ == "__main__":

@@ -130,6 +130,8 @@ def ring_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, C: int =
     dt = _dtype_code(q)
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k and v must share a dtype")
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q must be (tokens, h_q, d) and k, v (tokens, h_kv, d)")
     Tt, h_q, d = q.shape
     St, h_kv, dk = k.shape
     if v.shape != k.shape or dk != d:
@@ -173,8 +175,14 @@ def attn_partial(q, k, v, *, q_pos0: int = 0, k_pos0: int = 0, causal: bool = Fa
     place and the same tensors are returned."""
     dev = _dev(q, k, v)
     dt = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share a dtype")
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q must be (T, h_q, d) and k, v (n, h_kv, d)")
     T, h_q, d = q.shape
-    n, h_kv, _ = k.shape
+    n, h_kv, dk = k.shape
+    if v.shape != k.shape or dk != d:
+        raise ValueError("shape mismatch between q, k and v")
     if state is None:
         m = torch.empty((T, h_q), dtype=torch.float32, device=dev)
         l = torch.empty((T, h_q), dtype=torch.float32, device=dev)
@@ -197,6 +205,12 @@ def attn_partial(q, k, v, *, q_pos0: int = 0, k_pos0: int = 0, causal: bool = Fa
 def lse_merge(m_parts, l_parts, o_parts, *, out_dtype=torch.bfloat16, return_lse: bool = False):
     """Merge n triplets per row: m/l (n, rows), O (n, rows, d) -> O / l (rows, d)."""
     dev = _dev(m_parts, l_parts, o_parts)
+    if any(t.dtype != torch.float32 for t in (m_parts, l_parts, o_parts)):
+        raise TypeError("m_parts, l_parts and o_parts must be float32")
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"out_dtype must be torch.bfloat16 or torch.float32, got {out_dtype}")
+    if o_parts.dim() != 3:
+        raise ValueError("o_parts must be (n_parts, rows, d)")
     n, rows, d = o_parts.shape
     if m_parts.shape != (n, rows) or l_parts.shape != (n, rows):
         raise ValueError("m_parts and l_parts must be (n_parts, rows)")
@@ -213,6 +227,10 @@ def splitkv_decode(q, k, v, *, n_chunks: int, workspace: Optional[torch.Tensor] 
     """One decode step: q (B, h_q, d), K/V cache (B, S, h_kv, d) -> o (B, h_q, d)."""
     dev = _dev(q, k, v)
     dt = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share a dtype")
+    if q.dim() != 3 or k.dim() != 4:
+        raise ValueError("q must be (B, h_q, d) and k, v (B, S, h_kv, d)")
     B, h_q, d = q.shape
     Bk, S, h_kv, dk = k.shape
     if Bk != B or dk != d or v.shape != k.shape:

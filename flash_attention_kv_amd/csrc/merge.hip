@@ -6,7 +6,9 @@
 // all n parts of a row at once it reads: m' = max_c m_c, l' = sum_c l_c
 // exp(m_c - m'), O' = sum_c O_c exp(m_c - m') -- the root of a one-level merge
 // tree, equal in exact arithmetic to any pairwise order.  Parts with
-// m = -inf (empty chunks) get weight 0.
+// m = -inf (empty chunks) get weight 0.  A row whose parts are all empty
+// merges to the identity (-inf, 0, 0): its output row is written as zeros and
+// its lse as -inf (ln of an empty sum), never 0/0.
 //
 // One workgroup per row: thread t owns 4 consecutive dims (t mod D/4) of the
 // parts c = g, g + G, g + 2G, ... of part group g = t / (D/4), G = 1024/D.
@@ -63,14 +65,14 @@ void lse_merge_kernel(MergeParams p) {
     l += s_l[q];
     o += s_o[q][t];
   }
-  const float inv = 1.f / l;
+  const float inv = l > 0.f ? 1.f / l : 0.f;   // all parts empty: O' = 0, written as 0
   if (p.out_bf16) {
     u32x2 x = {pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
     *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.o_out) + row * D + 4 * t) = x;
   } else {
     *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.o_out) + row * D + 4 * t) = o * inv;
   }
-  if (p.lse_out != nullptr && t == 0) p.lse_out[row] = M + logf(l);
+  if (p.lse_out != nullptr && t == 0) p.lse_out[row] = l > 0.f ? M + logf(l) : neg_inf();
 }
 
 template <int D>

@@ -12,8 +12,12 @@
 // One workgroup of 1024 threads: for t = T-1 .. 0 it ranks the sequences with
 // more than t tiles by a block-wide prefix count (wave ballots + popcounts)
 // and scatters their records.  Offsets that are not a valid prefix array
-// (first != 0, decreasing, last != total) yield an empty list, so a bad
-// argument can never make the prefill kernel read out of bounds.
+// (first != 0, a decreasing pair, last != total) yield an empty list, so a
+// bad argument can never make the prefill kernel read out of bounds.  Each
+// pair is validated by a direct compare, never by the sign of a difference:
+// a difference of two arbitrary int32 values can wrap to a positive length.
+// Once every pair is non-decreasing from 0 to total, all offsets lie in
+// [0, total] and no length computed from them can wrap.
 #include "fakv_device.h"
 #include "fakv_kernels.h"
 
@@ -32,10 +36,12 @@ void worklist_kernel(const int32_t* __restrict__ off, int n_seqs, int total, int
   __syncthreads();
   int local_max = 0, bad = 0;
   for (int b = tid; b < n_seqs; b += 1024) {
-    const int L = off[b + 1] - off[b];
+    const int a0 = off[b], a1 = off[b + 1];
+    if (a1 < a0) bad = 1;
+    // (only used when every pair is ordered, so then 0 <= L <= total)
+    const int L = bad ? 0 : a1 - a0;
     if (b < kCache) s_len[b] = L;
-    if (L < 0) bad = 1;
-    local_max = max(local_max, (max(L, 0) + BQ - 1) / BQ);
+    local_max = max(local_max, L / BQ + (L % BQ != 0));
   }
   // the ranking passes below revisit every sequence once per tile index:
   // lengths come from LDS, not from global offsets, on that path
@@ -159,8 +165,12 @@ void schedule_kernel(const int32_t* __restrict__ off, int n_seqs, int BQ, const 
     if (tid < 16) sb.qinfo[tid] = 0;
     return;
   }
-  // (offsets are a valid prefix array here: worklist_kernel checked them)
-  auto ntiles = [&](int b) { return (off[b + 1] - off[b] + BQ - 1) / BQ; };
+  // (offsets are a valid prefix array here: worklist_kernel checked every
+  // pair by direct compares, so 0 <= L <= total and L cannot wrap)
+  auto ntiles = [&](int b) {
+    const int L = off[b + 1] - off[b];
+    return L / BQ + (L % BQ != 0);
+  };
   auto bin = [&](int v) { return min(v, 1024); };
 
   // 1. exclusive prefix sums of tiles per sequence; histogram of tile counts

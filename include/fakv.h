@@ -97,8 +97,9 @@ fakv_status attn_partial(const void* q, const void* k, const void* v,
  * exp(m_c - m') and the l's and O's are summed in a fixed order (a part with
  * m = -inf weighs 0), so results are reproducible.  Then O / l is written to
  * o_out (rows, d) in out_dtype, and
- * m + ln l to lse_out (rows) unless lse_out is NULL.  A row whose merged l is
- * 0 (every part empty) yields NaN output; callers never produce one.
+ * m + ln l to lse_out (rows) unless lse_out is NULL.  A row whose parts are
+ * all empty (every m = -inf, l = 0) merges to the identity triplet: its output
+ * row is written as zeros and its lse as -inf (the log of an empty sum).
  * This is the merge of the decode page's per-rank triplets and of the prefill
  * page's ring steps.  Preconditions: n_parts >= 1, rows >= 0.
  */

@@ -21,7 +21,7 @@ def test_more_than_one_gpu_is_refused():
 
 def test_traffic_follows_the_kernel_sources(tmp_path, monkeypatch):
     (tmp_path / "profiles").mkdir()
-    (tmp_path / "profiles" / "traffic.json").write_text(json.dumps({
+    (tmp_path / "profiles" / "counters.json").write_text(json.dumps({
         "gqa_ring": {"csrc_hash": "aaaa", "bytes_per_launch": 123},
         "decode": {"csrc_hash": "bbbb", "bytes_per_launch": 456}}))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))

@@ -180,3 +180,58 @@ def test_hand_fixtures():
 def test_empty_row_is_rejected():
     with pytest.raises(ValueError):
         oracle.attention_ref(np.zeros((2, 1, 2)), np.zeros((0, 1, 2)), np.zeros((0, 1, 2)))
+
+
+def _brute_rows(q, k, v, toks, heads, causal, segs, window=None):
+    """Rows (tokens[n], heads[n]) by pure-Python brute force, one sequence at a
+    time: segs = [(q0, q1, k0, k1)] of the packed batch."""
+    out = []
+    for t, h in zip(toks, heads):
+        q0, q1, k0, k1 = next(s for s in segs if s[0] <= t < s[1])
+        full = brute_attention(q[q0:q1].tolist(), k[k0:k1].tolist(), v[k0:k1].tolist(), causal, window)
+        out.append(full[t - q0][h])
+    return np.array(out)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_rows_ref_dense_batch_brute_force(causal):
+    """attention_rows_ref on a dense batch of 3 sequences (GQA 4/2): each row
+    is attention over its own sequence only, with sequence-local positions."""
+    n, L, d = 3, 6, 4
+    q, k, v = _rand((n * L, 4, d), 44), _rand((n * L, 2, d), 45), _rand((n * L, 2, d), 46)
+    toks = [0, 5, 6, 7, 11, 12, 17, 9]
+    heads = [0, 3, 1, 2, 3, 0, 3, 1]
+    segs = [(b * L, (b + 1) * L, b * L, (b + 1) * L) for b in range(n)]
+    got = oracle.attention_rows_ref(q, k, v, toks, heads, causal=causal, n_seqs=n)
+    np.testing.assert_allclose(got, _brute_rows(q, k, v, toks, heads, causal, segs), rtol=1e-12, atol=1e-13)
+    full = oracle.attention_ref(q, k, v, causal=causal, n_seqs=n)
+    np.testing.assert_allclose(got, full[toks, heads], rtol=1e-13, atol=1e-14)
+
+
+def test_rows_ref_rectangular_noncausal_brute_force():
+    """Non-causal rows of a dense batch with more keys than queries per
+    sequence (T_q = 3, S_kv = 7 each): the query and key ranges differ."""
+    n, Tq, Sk, d = 2, 3, 7, 5
+    q, k, v = _rand((n * Tq, 2, d), 47), _rand((n * Sk, 1, d), 48), _rand((n * Sk, 1, d), 49)
+    toks, heads = [0, 2, 3, 5, 4], [0, 1, 1, 0, 0]
+    segs = [(b * Tq, (b + 1) * Tq, b * Sk, (b + 1) * Sk) for b in range(n)]
+    got = oracle.attention_rows_ref(q, k, v, toks, heads, causal=False, n_seqs=n)
+    np.testing.assert_allclose(got, _brute_rows(q, k, v, toks, heads, False, segs), rtol=1e-12, atol=1e-13)
+    full = oracle.attention_ref(q, k, v, causal=False, n_seqs=n)
+    np.testing.assert_allclose(got, full[toks, heads], rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("window", [1, 2, 4, 9])
+def test_rows_ref_window_brute_force(window):
+    """Sliding-window rows (query i sees i - W < j <= i) on a dense batch of
+    two sequences and on a jagged batch, against brute force."""
+    d = 3
+    q, k, v = _rand((16, 2, d), 50 + window), _rand((16, 1, d), 60 + window), _rand((16, 1, d), 70 + window)
+    toks, heads = [0, 3, 7, 8, 12, 15], [0, 1, 1, 0, 1, 0]
+    segs = [(0, 8, 0, 8), (8, 16, 8, 16)]
+    got = oracle.attention_rows_ref(q, k, v, toks, heads, causal=True, n_seqs=2, window=window)
+    np.testing.assert_allclose(got, _brute_rows(q, k, v, toks, heads, True, segs, window), rtol=1e-12, atol=1e-13)
+    offs = [0, 5, 5, 16]
+    jsegs = [(0, 5, 0, 5), (5, 16, 5, 16)]
+    gotj = oracle.attention_rows_ref(q, k, v, toks, heads, causal=True, seq_offsets=offs, window=window)
+    np.testing.assert_allclose(gotj, _brute_rows(q, k, v, toks, heads, True, jsegs, window), rtol=1e-12, atol=1e-13)

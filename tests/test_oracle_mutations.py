@@ -113,3 +113,49 @@ def test_window_lower_bound_too_late_is_caught(monkeypatch):
     for C, W in ((1, 17), (4, 64), (3, 5)):
         with pytest.raises((AssertionError, ValueError)):
             WIN.test_window_ring_equals_monolithic(C, W)
+
+
+def test_decode_flops_half_count_is_caught(monkeypatch):
+    monkeypatch.setattr(oracle, "decode_flops", lambda B, h_q, d, S: 2 * d * h_q * B * S)
+    _fails(WD.test_decode_counts_brute_force)
+
+
+def _rows_ref_variant(local_index: bool = True, keys_from_queries: bool = False, use_window: bool = True):
+    """attention_rows_ref with one planted slip: a global instead of a
+    sequence-local query index, key ranges taken from the query ranges, or
+    the window dropped."""
+    from oracle._util import f64, segments
+
+    def rows(q, k, v, tokens, heads, *, causal=False, n_seqs=1, seq_offsets=None, window=None):
+        T, h_q, d = q.shape
+        S, h_kv, _ = k.shape
+        segs = segments(T, S, n_seqs, seq_offsets)
+        res = np.zeros((len(tokens), d))
+        for n, (t, h) in enumerate(zip(tokens, heads)):
+            q0, q1, k0, k1 = next(s for s in segs if s[0] <= t < s[1])
+            if keys_from_queries:
+                k0, k1 = q0, q1
+            kv = oatt.kv_head_of(int(h), h_q, h_kv)
+            qr = f64(q[t, h]).reshape(1, d)
+            kk, vv = f64(k[k0:k1, kv]), f64(v[k0:k1, kv])
+            ii = np.array([t - q0 if local_index else t])
+            allowed = oatt.admissible(ii, np.arange(k1 - k0), causal, window if use_window else None)
+            res[n] = oatt._attend(qr, kk, vv, allowed, oatt.softmax_scale(d))[0][0]
+        return res
+    return rows
+
+
+def test_rows_ref_global_index_is_caught(monkeypatch):
+    monkeypatch.setattr(oracle, "attention_rows_ref", _rows_ref_variant(local_index=False))
+    _fails(A.test_rows_ref_dense_batch_brute_force, True)
+
+
+def test_rows_ref_key_range_is_caught(monkeypatch):
+    monkeypatch.setattr(oracle, "attention_rows_ref", _rows_ref_variant(keys_from_queries=True))
+    with pytest.raises((AssertionError, ValueError)):
+        A.test_rows_ref_rectangular_noncausal_brute_force()
+
+
+def test_rows_ref_dropped_window_is_caught(monkeypatch):
+    monkeypatch.setattr(oracle, "attention_rows_ref", _rows_ref_variant(use_window=False))
+    _fails(A.test_rows_ref_window_brute_force, 2)

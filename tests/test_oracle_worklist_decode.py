@@ -108,6 +108,29 @@ def test_counts_closed_forms_and_brute_force():
     assert oracle.decode_bytes(1, 2, 1, 4, 10) == 2 * 10 * 4 * 2 + 2 * 2 * 4 * 2
 
 
+def test_decode_counts_brute_force():
+    """decode_flops and decode_bytes against an enumeration: every (sequence,
+    query head, cached key) pair costs d multiply-adds for its score and d for
+    its value product (2 FLOP each); every K and V element of the cache is
+    read once and every q and o element moved once."""
+    import oracle
+    for (B, h_q, h_kv, d, S) in [(1, 1, 1, 1, 1), (2, 4, 2, 3, 5), (3, 6, 3, 2, 7)]:
+        flops = 0
+        for _b in range(B):
+            for _h in range(h_q):
+                for _j in range(S):
+                    flops += 2 * d      # score: d multiplies + d adds
+                    flops += 2 * d      # value: d multiplies + d adds
+        assert oracle.decode_flops(B, h_q, d, S) == flops
+        # one query per sequence, every cached key admissible: the prefill count
+        pairs = oracle.prefill_pairs(B, B * S, causal=False, n_seqs=B)
+        assert oracle.decode_flops(B, h_q, d, S) == oracle.useful_flops_prefill(h_q, d, pairs)
+        elems = sum(1 for _t in ("k", "v") for _b in range(B) for _j in range(S) for _h in range(h_kv)
+                    for _x in range(d))
+        elems += sum(1 for _t in ("q", "o") for _b in range(B) for _h in range(h_q) for _x in range(d))
+        assert oracle.decode_bytes(B, h_q, h_kv, d, S) == 2 * elems
+
+
 def test_workload_sizes():
     w = WORKLOADS["jagged"]
     offs = seq_offsets_from_lengths(jagged_lengths(w.n_seqs))
