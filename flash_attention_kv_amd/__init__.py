@@ -9,8 +9,10 @@ binding: PyTorch supplies device memory and the HIP stream only.
 """
 from ._binding import (F32, BF16, FakvError, LIB_PATH, SIGNATURES, lib, ring_attn_fwd,
                        attn_partial, lse_merge, splitkv_decode, jagged_worklist, query_tile_rows,
-                       ring_attn_workspace_bytes, splitkv_decode_workspace_bytes)
+                       ring_attn_workspace_bytes, splitkv_decode_workspace_bytes,
+                       splitkv_decode_noalloc, DECODE_SCRATCH_BYTES)
 
 __all__ = ["F32", "BF16", "FakvError", "LIB_PATH", "SIGNATURES", "lib", "ring_attn_fwd",
            "attn_partial", "lse_merge", "splitkv_decode", "jagged_worklist", "query_tile_rows",
-           "ring_attn_workspace_bytes", "splitkv_decode_workspace_bytes"]
+           "ring_attn_workspace_bytes", "splitkv_decode_workspace_bytes",
+           "splitkv_decode_noalloc", "DECODE_SCRATCH_BYTES"]

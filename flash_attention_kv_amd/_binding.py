@@ -30,6 +30,7 @@ SIGNATURES = {
     "ring_attn_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I, _I, _I]),
     "splitkv_decode": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _SZ, _P]),
     "splitkv_decode_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
+    "splitkv_decode_noalloc": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "fakv_jagged_worklist": (_I, [_P, _I, _I, _I, _P, _P, _SZ, _P]),
     "fakv_query_tile_rows": (_I, [_I, _I, _I, _I]),
     "fakv_last_error": (ctypes.c_char_p, []),
@@ -244,6 +245,32 @@ def splitkv_decode(q, k, v, *, n_chunks: int, workspace: Optional[torch.Tensor] 
     st = lib().splitkv_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, h_q, h_kv, d, S, n_chunks, dt,
                               _ptr(workspace), need, _stream(dev))
     _check("splitkv_decode", st)
+    return o
+
+
+# bytes of the per-device scratch splitkv_decode_noalloc uses (FAKV_DECODE_SCRATCH_BYTES)
+DECODE_SCRATCH_BYTES = 32 << 20
+
+
+def splitkv_decode_noalloc(q, k, v, *, n_chunks: int, out: torch.Tensor):
+    """splitkv_decode with the library's own per-device scratch for the
+    partial triplets: no workspace, and the caller passes the output, so the
+    call allocates nothing.  Calls that may overlap on one device race on
+    that scratch (serialise them, e.g. on one stream)."""
+    dev = _dev(q, k, v)
+    dt = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share a dtype")
+    if q.dim() != 3 or k.dim() != 4:
+        raise ValueError("q must be (B, h_q, d) and k, v (B, S, h_kv, d)")
+    B, h_q, d = q.shape
+    Bk, S, h_kv, dk = k.shape
+    if Bk != B or dk != d or v.shape != k.shape:
+        raise ValueError("shape mismatch between q, k and v")
+    o = _out_like(out, q)
+    st = lib().splitkv_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, h_q, h_kv, d, S, n_chunks, dt,
+                                      _stream(dev))
+    _check("splitkv_decode_noalloc", st)
     return o
 
 

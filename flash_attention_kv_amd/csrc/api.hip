@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "fakv.h"
@@ -233,9 +234,42 @@ static fakv_status ring_attn_impl(const void* q, const void* k, const void* v, v
   return launch_prefill(p, d, dtype, fakv::prefill_bf16_persistent_grid(d, qh), st);
 }
 
+// ---------------------------------------------------------------------------
+// Library-owned scratch of splitkv_decode_noalloc: the decode partial
+// triplets live in this device array instead of a caller workspace.  Each
+// device that runs the library holds its own copy (FAKV_DECODE_SCRATCH_BYTES)
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory, so host code never uses it directly: the device address
+// of each device's copy is looked up once, with that device current, and kept
+// in g_scratch_ptr[device].
+static __device__ __align__(256) char scratch[FAKV_DECODE_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up on first use).
+fakv_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_fail("hipGetDevice", e);
+  if (dev < 0 || dev >= kMaxDevices) return fail(FAKV_EUNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) return device_fail("hipGetSymbolAddress(scratch)", e);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FAKV_OK;
+}
+}  // namespace
+
 extern "C" {
 
-int fakv_abi_version(void) { return 101; }
+int fakv_abi_version(void) { return 102; }
 
 const char* fakv_last_error(void) { return g_err.c_str(); }
 
@@ -324,10 +358,11 @@ fakv_status ring_attn_fwd_window(const void* q, const void* k, const void* v, vo
                         workspace, workspace_bytes, stream);
 }
 
-fakv_status splitkv_decode(const void* q, const void* k, const void* v, void* o, int B, int h_q,
-                           int h_kv, int d, int S_kv, int n_chunks, int dtype, void* workspace,
-                           size_t workspace_bytes, void* stream) {
-  g_err.clear();
+}  // extern "C"
+
+// Argument checks shared by splitkv_decode and splitkv_decode_noalloc.
+static fakv_status check_decode(const void* q, const void* k, const void* v, void* o, int B, int h_q,
+                                int h_kv, int d, int S_kv, int n_chunks, int dtype) {
   fakv_status s = check_prefill_common(q, k, v, h_q, h_kv, d, dtype);
   if (s != FAKV_OK) return s;
   if (!o) return fail(FAKV_EINVAL, "o must be non-null");
@@ -341,12 +376,14 @@ fakv_status splitkv_decode(const void* q, const void* k, const void* v, void* o,
   if ((long long)B * h_q >= (1ll << 31)) return fail(FAKV_EINVAL, "B * h_q exceeds int32");
   if ((s = check_kv_extent(S_kv, h_kv, d, dtype)) != FAKV_OK) return s;
   if ((long long)B * h_kv * n_chunks > 0x7fffffffll) return fail(FAKV_EINVAL, "grid too large");
-  const size_t need = splitkv_decode_workspace_bytes(B, h_q, d, n_chunks);
-  if (workspace == nullptr || workspace_bytes < need)
-    return fail(FAKV_EINVAL, "workspace too small: need %zu bytes, got %zu", need, workspace_bytes);
-  if (!aligned16(workspace)) return fail(FAKV_EINVAL, "workspace must be 16-byte aligned");
+  return FAKV_OK;
+}
+
+// Enqueues the partial and merge kernels of a checked decode call; the
+// partial triplets go to ws (at least splitkv_decode_workspace_bytes bytes).
+static fakv_status enqueue_decode(const void* q, const void* k, const void* v, void* o, int B, int h_q,
+                                  int h_kv, int d, int S_kv, int n_chunks, char* ws, void* stream) {
   const size_t parts = (size_t)n_chunks * B * h_q;
-  char* ws = static_cast<char*>(workspace);
   fakv::DecodeParams p{};
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
@@ -365,6 +402,37 @@ fakv_status splitkv_decode(const void* q, const void* k, const void* v, void* o,
   e = fakv::launch_lse_merge(mp, d, st);
   if (e != hipSuccess) return device_fail("decode merge launch", e);
   return FAKV_OK;
+}
+
+extern "C" {
+
+fakv_status splitkv_decode(const void* q, const void* k, const void* v, void* o, int B, int h_q,
+                           int h_kv, int d, int S_kv, int n_chunks, int dtype, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  fakv_status s = check_decode(q, k, v, o, B, h_q, h_kv, d, S_kv, n_chunks, dtype);
+  if (s != FAKV_OK) return s;
+  const size_t need = splitkv_decode_workspace_bytes(B, h_q, d, n_chunks);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(FAKV_EINVAL, "workspace too small: need %zu bytes, got %zu", need, workspace_bytes);
+  if (!aligned16(workspace)) return fail(FAKV_EINVAL, "workspace must be 16-byte aligned");
+  return enqueue_decode(q, k, v, o, B, h_q, h_kv, d, S_kv, n_chunks, static_cast<char*>(workspace), stream);
+}
+
+fakv_status splitkv_decode_noalloc(const void* q, const void* k, const void* v, void* o, int B, int h_q,
+                                   int h_kv, int d, int S_kv, int n_chunks, int dtype, void* stream) {
+  g_err.clear();
+  fakv_status s = check_decode(q, k, v, o, B, h_q, h_kv, d, S_kv, n_chunks, dtype);
+  if (s != FAKV_OK) return s;
+  const size_t need = splitkv_decode_workspace_bytes(B, h_q, d, n_chunks);
+  if (need > (size_t)FAKV_DECODE_SCRATCH_BYTES)
+    return fail(FAKV_EINVAL,
+                "splitkv_decode_noalloc: partials of n_chunks * B * h_q * (d + 2) fp32 need %zu bytes, "
+                "beyond the library's %zu-byte scratch; use splitkv_decode with a workspace",
+                need, (size_t)FAKV_DECODE_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((s = scratch_of_current_device(&ws)) != FAKV_OK) return s;
+  return enqueue_decode(q, k, v, o, B, h_q, h_kv, d, S_kv, n_chunks, static_cast<char*>(ws), stream);
 }
 
 fakv_status fakv_jagged_worklist(const int32_t* seq_offsets, int n_seqs, int total_tokens, int BQ,

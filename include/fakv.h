@@ -184,6 +184,31 @@ fakv_status splitkv_decode(const void* q, const void* k, const void* v, void* o,
 
 size_t splitkv_decode_workspace_bytes(int B, int h_q, int d, int n_chunks);
 
+/* Bytes of device scratch the library itself holds per device for
+ * splitkv_decode_noalloc (32 MiB). */
+#define FAKV_DECODE_SCRATCH_BYTES (32u << 20)
+
+/*
+ * splitkv_decode_noalloc -- splitkv_decode without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * layouts, kernels, results and errors as splitkv_decode, except that the
+ * partial triplets go to a scratch array the library holds on each device
+ * (FAKV_DECODE_SCRATCH_BYTES, allocated with the library's code on that
+ * device and kept until the process ends).  The call itself allocates and
+ * frees nothing; its first call on a device looks up that device's scratch
+ * address.  A call whose partials need more than the scratch
+ * (splitkv_decode_workspace_bytes(B, h_q, d, n_chunks) >
+ * FAKV_DECODE_SCRATCH_BYTES) returns FAKV_EINVAL and enqueues nothing.
+ * Every call on one device shares that scratch, and every call overwrites
+ * all of the triplets it reads: calls that may overlap on one device (on
+ * different streams, or from several threads) race and must be serialised
+ * by the caller, e.g. on one stream.
+ */
+fakv_status splitkv_decode_noalloc(const void* q, const void* k, const void* v, void* o,
+                                   int B, int h_q, int h_kv, int d, int S_kv, int n_chunks,
+                                   int dtype, void* stream);
+
 /*
  * fakv_jagged_worklist -- build the flattened (sequence, query-tile) worklist
  * of a jagged batch on the device ("Flattened worklists" of the Helion page):
@@ -208,7 +233,7 @@ int fakv_query_tile_rows(int h_q, int h_kv, int d, int dtype);
  * Valid until the next library call on that thread. */
 const char* fakv_last_error(void);
 
-/* ABI version of this header (major * 100 + minor): 101. */
+/* ABI version of this header (major * 100 + minor): 102. */
 int fakv_abi_version(void);
 
 #ifdef __cplusplus

@@ -31,7 +31,7 @@ def test_header_symbols_exported():
 
 def test_version_and_tile_rows():
     L = F.lib()
-    assert L.fakv_abi_version() == 101
+    assert L.fakv_abi_version() == 102
     # jagged bf16 tiles: 8 waves of 32 rows, split over the query heads that
     # share a KV tile
     assert F.query_tile_rows(32, 8, 128) == 64      # 4 query heads share a KV tile
@@ -143,3 +143,21 @@ def test_kv_span_limit():
     ws = F.splitkv_decode_workspace_bytes(1, 64, 256, 64)
     assert L.splitkv_decode(16, 16, 16, 16, 1, 64, 64, 256, 65536, 64, F.BF16, 16, ws, None) == EUNSUP
     assert b"2 GiB" in L.fakv_last_error()
+
+
+def test_noalloc_decode_rejects_before_any_hip_call():
+    """splitkv_decode_noalloc applies splitkv_decode's checks and refuses a
+    call whose partial triplets would not fit the library's scratch, all on
+    the host (no device is touched)."""
+    L = F.lib()
+    assert L.splitkv_decode_noalloc(16, 16, 16, 16, 2, 8, 1, 128, 64, 4, F.F32, None) == EUNSUP
+    assert L.splitkv_decode_noalloc(16, 16, 16, 16, 2, 8, 1, 128, 64, 65, F.BF16, None) == EINVAL
+    assert L.splitkv_decode_noalloc(None, 16, 16, 16, 2, 8, 1, 128, 64, 4, F.BF16, None) == EINVAL
+    # the decode workload's partials (17 MB) fit; 64 more chunks do not
+    assert F.splitkv_decode_workspace_bytes(8, 64, 128, 64) <= F.DECODE_SCRATCH_BYTES
+    assert F.splitkv_decode_workspace_bytes(8, 64, 128, 128) > F.DECODE_SCRATCH_BYTES
+    assert L.splitkv_decode_noalloc(16, 16, 16, 16, 8, 64, 8, 128, 131072, 128, F.BF16, None) == EINVAL
+    assert b"scratch" in L.fakv_last_error()
+    header = open(HEADER).read()
+    assert "#define FAKV_DECODE_SCRATCH_BYTES (32u << 20)" in header
+    assert F.DECODE_SCRATCH_BYTES == 32 << 20
