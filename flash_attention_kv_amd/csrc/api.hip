@@ -64,6 +64,27 @@ size_t worklist_capacity(int total, int n_seqs, int BQ) {
   return (size_t)(total / BQ) + (size_t)n_seqs;
 }
 
+// Split-KV parts of an fp32 dense call (0 = one workgroup per query tile
+// walks the whole ring).  When the query tiles alone would occupy few CUs,
+// each ring chunk is cut into `sub` equal parts of at least one 32-key tile,
+// sub dividing the chunk width, enough to give ~256 workgroups in all.
+int f32_kv_parts(int T_q, int S_kv, int h_q, int n_seqs, int C) {
+  const long long grid = (long long)((T_q + fakv::kF32QueryTile - 1) / fakv::kF32QueryTile) * h_q * n_seqs;
+  if (grid >= 128 || C < 1 || S_kv % C) return 0;
+  const int w = S_kv / C;
+  const long long want = (256 + grid * C - 1) / (grid * C);
+  int sub = 1;
+  for (int t = 2; t <= w / 32 && t <= want; ++t)
+    if (w % t == 0) sub = t;
+  return C * sub > 1 ? C * sub : 0;
+}
+
+// fp32 split-KV workspace: [O parts][m parts][l parts].
+size_t f32_split_bytes(int parts, size_t rows, int d) {
+  const size_t n = (size_t)parts * rows;
+  return align256(n * d * 4) + 2 * align256(n * 4);
+}
+
 // Jagged-batch workspace: [header 256 B: n_items, queue info] [records]
 // and, for bf16, the per-XCD schedule arrays.
 struct JaggedLayout {
@@ -176,6 +197,14 @@ static fakv_status ring_attn_impl(const void* q, const void* k, const void* v, v
       return fail(FAKV_EINVAL, "token count exceeds int32");
     if ((s = check_kv_extent(S_kv, h_kv, d, dtype)) != FAKV_OK) return s;
     if (T_q == 0) return FAKV_OK;
+    const int parts = dtype == FAKV_F32 ? f32_kv_parts(T_q, S_kv, h_q, n_seqs, C) : 0;
+    const size_t rows = (size_t)n_seqs * T_q * h_q;
+    if (parts > 0) {
+      const size_t need = f32_split_bytes(parts, rows, d);
+      if (workspace == nullptr || workspace_bytes < need)
+        return fail(FAKV_EINVAL, "workspace too small: need %zu bytes, got %zu", need, workspace_bytes);
+      if (!aligned16(workspace)) return fail(FAKV_EINVAL, "workspace must be 16-byte aligned");
+    }
     fakv::PrefillParams p = base_params(q, k, v, h_q, h_kv, d);
     p.o = static_cast<uint16_t*>(o);
     p.mode = 0;
@@ -184,9 +213,23 @@ static fakv_status ring_attn_impl(const void* q, const void* k, const void* v, v
     p.window = window;
     p.n_qtiles = (T_q + BQ - 1) / BQ;
     p.n_hg = h_q / qh;
-    const long long grid = (long long)p.n_qtiles * p.n_hg * n_seqs;
+    const long long grid = (long long)p.n_qtiles * p.n_hg * n_seqs * (parts > 0 ? parts : 1);
     if (grid > 0x7fffffffll) return fail(FAKV_EINVAL, "grid too large");
-    return launch_prefill(p, d, dtype, (int)grid, st);
+    if (parts == 0) return launch_prefill(p, d, dtype, (int)grid, st);
+    // fp32 split-KV: one partial triplet per (query tile, part), then the merge
+    char* ws = static_cast<char*>(workspace);
+    const size_t n = (size_t)parts * rows;
+    p.mode = 1;
+    p.kv_parts = parts;
+    p.o_st = reinterpret_cast<float*>(ws);
+    p.m_st = reinterpret_cast<float*>(ws + align256(n * d * 4));
+    p.l_st = reinterpret_cast<float*>(ws + align256(n * d * 4) + align256(n * 4));
+    if ((s = launch_prefill(p, d, dtype, (int)grid, st)) != FAKV_OK) return s;
+    if (rows > 0x7fffffffull) return fail(FAKV_EINVAL, "too many rows");
+    fakv::MergeParams mp{p.m_st, p.l_st, p.o_st, parts, (int)rows, o, nullptr, 0};
+    hipError_t e = fakv::launch_lse_merge(mp, d, st);
+    if (e != hipSuccess) return device_fail("split-KV merge launch", e);
+    return FAKV_OK;
   }
   // jagged batch
   if (T_q != S_kv) return fail(FAKV_EINVAL, "a jagged batch needs T_q == S_kv == total tokens");
@@ -280,8 +323,12 @@ int fakv_query_tile_rows(int h_q, int h_kv, int d, int dtype) {
 
 size_t ring_attn_workspace_bytes(int T_q, int S_kv, int h_q, int h_kv, int d, int C, int causal,
                                  int n_seqs, int jagged, int dtype) {
-  (void)S_kv; (void)C; (void)causal;
-  if (!jagged || T_q <= 0 || n_seqs < 1 || h_q < 1 || h_kv < 1 || h_q % h_kv || !supported_d(d)) return 0;
+  (void)causal;
+  if (T_q <= 0 || n_seqs < 1 || h_q < 1 || h_kv < 1 || h_q % h_kv || !supported_d(d)) return 0;
+  if (!jagged) {
+    const int parts = dtype == FAKV_F32 ? f32_kv_parts(T_q, S_kv, h_q, n_seqs, C) : 0;
+    return parts > 0 ? f32_split_bytes(parts, (size_t)n_seqs * T_q * h_q, d) : 0;
+  }
   const int BQ = query_tile(h_q, h_kv, d, dtype, true);
   const bool bf16 = dtype == FAKV_BF16;
   const int n_hg = bf16 ? h_q / heads_per_wg(h_q, h_kv) : h_q;

@@ -183,6 +183,7 @@ struct KvWalk {
   int prune;
   int BK;
   int lo;         // sliding window: first key the tile's first row admits (else very negative)
+  int single;     // visit chunk r only (one part of a split-KV partial), not the whole ring
   // state
   int s;          // ring step of the current chunk
   int c0, c1;     // current chunk's key range
@@ -206,13 +207,15 @@ struct KvWalk {
   __device__ __forceinline__ void first() {
     s = 0;
     valid = 0;
-    for (; s < C; ++s)
+    const int n = single ? 1 : C;
+    for (; s < n; ++s)
       if (open_chunk()) { valid = 1; return; }
   }
   __device__ __forceinline__ void next() {
     kt += BK;
     if (kt < end) return;
-    for (++s; s < C; ++s)
+    const int n = single ? 1 : C;
+    for (++s; s < n; ++s)
       if (open_chunk()) return;
     valid = 0;
   }

@@ -34,6 +34,8 @@ struct PrefillParams {
   float scale;             // 1 / sqrt(d)
   float scale_log2;        // scale * log2(e)
   int window;              // causal sliding window in keys (query i sees i - window < j <= i); 0 = none
+  int kv_parts;            // fp32 dense split-KV: workgroups per query tile, one KV part each
+                           // (mode 1 triplets at part * rows); 0 = one workgroup walks the ring
 };
 
 struct DecodeParams {

@@ -99,6 +99,7 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
   walk.r = (Lq > 0) ? (int)(((long long)q_lo * p.C) / Lq) : 0;
   walk.q_hi = q_hi; walk.delta = delta; walk.causal = p.causal; walk.prune = p.prune;
   walk.BK = BK;
+  walk.single = 0;
   // sliding window W (causal): key j is admissible for query i iff
   // i - W < j <= i; the walk starts at the tile holding the first row's first key
   const int win = p.causal ? p.window : 0;

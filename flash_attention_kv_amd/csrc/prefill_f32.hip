@@ -7,6 +7,14 @@
 // single k-value per operand, so V needs no transposition: for the value
 // product O^T += V^T P^T the lane's own P register is the B operand and V is
 // read row-major.  One workgroup = 4 waves = 128 query rows of one head.
+//
+// Split-KV mode (kv_parts = P > 0, dense batches): the ring's C chunks are cut
+// into P equal parts (P a multiple of C, so every part lies inside one ring
+// chunk) and each workgroup computes the partial triplet of one (query tile,
+// part) -- the prefill page's per-chunk partial, spread over P workgroups
+// instead of walked by one -- writing it at part * rows of the triplet
+// arrays; lse_merge then folds the P parts of every row.  Small problems (one
+// 128-row tile against a few hundred keys) otherwise leave all but one CU idle.
 #include "fakv_device.h"
 #include "fakv_kernels.h"
 
@@ -36,6 +44,11 @@ void prefill_f32_kernel(PrefillParams p) {
   const int half = lane >> 5, col = lane & 31;
 
   int seq_q0, seq_k0, Lq, Lk, q_lo, q_hi, head;
+  int part = 0, wg = blockIdx.x;
+  if (p.kv_parts > 0) {
+    part = wg % p.kv_parts;
+    wg /= p.kv_parts;
+  }
   if (p.items != nullptr) {
     const int item = blockIdx.x / p.n_hg;
     head = blockIdx.x - item * p.n_hg;
@@ -47,8 +60,8 @@ void prefill_f32_kernel(PrefillParams p) {
     q_hi = it[6] - it[2];
   } else {
     const int pairs = p.n_seqs * p.n_hg;
-    const int qt_rev = blockIdx.x / pairs;
-    const int pair = blockIdx.x - qt_rev * pairs;
+    const int qt_rev = wg / pairs;
+    const int pair = wg - qt_rev * pairs;
     const int qt = p.n_qtiles - 1 - qt_rev;
     const int seq = pair / p.n_hg;
     head = pair - seq * p.n_hg;
@@ -66,6 +79,13 @@ void prefill_f32_kernel(PrefillParams p) {
   walk.r = (Lq > 0) ? (int)(((long long)q_lo * p.C) / Lq) : 0;
   walk.q_hi = q_hi; walk.delta = delta; walk.causal = p.causal; walk.prune = p.prune;
   walk.BK = BK;
+  walk.single = 0;
+  if (p.kv_parts > 0) {          // this workgroup's part only
+    walk.C = p.kv_parts;
+    walk.w = Lk / p.kv_parts;
+    walk.r = part;
+    walk.single = 1;
+  }
   // sliding window W (causal): key j is admissible for query i iff
   // i - W < j <= i; the walk starts at the tile holding the first row's first key
   const int win = p.causal ? p.window : 0;
@@ -194,6 +214,15 @@ void prefill_f32_kernel(PrefillParams p) {
 
   const float l_tot = l_run + xor32(l_run);
   if (!qvalid) return;
+  float* m_st = p.m_st;
+  float* l_st = p.l_st;
+  float* o_st = p.o_st;
+  if (p.kv_parts > 0) {
+    const size_t rows = (size_t)p.n_seqs * p.T_q * p.h_q;
+    m_st += part * rows;
+    l_st += part * rows;
+    o_st += part * rows * D;
+  }
   if (p.mode == 0) {
     const float inv = 1.f / l_tot;
     float* op = reinterpret_cast<float*>(p.o) + qrow * D + 4 * half;
@@ -206,8 +235,8 @@ void prefill_f32_kernel(PrefillParams p) {
         *reinterpret_cast<f32x4*>(op + 32 * b + 8 * g) = x;
       }
   } else {
-    if (half == 0) { p.m_st[qrow] = m_run; p.l_st[qrow] = l_tot; }
-    float* os = p.o_st + qrow * D + 4 * half;
+    if (half == 0) { m_st[qrow] = m_run; l_st[qrow] = l_tot; }
+    float* os = o_st + qrow * D + 4 * half;
 #pragma unroll
     for (int b = 0; b < DB; ++b)
 #pragma unroll

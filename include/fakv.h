@@ -125,7 +125,10 @@ fakv_status lse_merge(const float* m_parts, const float* l_parts, const float* o
  *   read or written out of bounds).
  * Each query tile takes the ring position of its first row, r = floor(i*C/L),
  * and visits KV chunks in the order (r + s) mod C, s = 0..C-1, as the prefill
- * page's rank r does after s westward rotations.  Causal: a chunk starting at
+ * page's rank r does after s westward rotations.  (A small fp32 dense call
+ * instead computes the partial triplet of every chunk -- cut into equal parts
+ * -- in separate workgroups and merges them in part order; see
+ * ring_attn_workspace_bytes.)  Causal: a chunk starting at
  * or after the tile's end is skipped whole, and inside a chunk the key loop
  * ends at min(chunk end, query tile end) ("dependent Tile.end"), so only the
  * tiles straddling the diagonal apply an element mask.
@@ -157,7 +160,11 @@ fakv_status ring_attn_fwd_window(const void* q, const void* k, const void* v, vo
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace needed by ring_attn_fwd for these arguments (jagged = seq_offsets
- * != NULL).  0 for dense batches. */
+ * != NULL).  Dense bf16 batches need none (0).  A dense fp32 call whose query
+ * tiles would occupy few compute units is split over its KV range -- each
+ * ring chunk cut into equal parts, one partial triplet per (query tile,
+ * part), merged by the lse_merge kernel -- and needs room for those fp32
+ * triplets; larger fp32 calls need none. */
 size_t ring_attn_workspace_bytes(int T_q, int S_kv, int h_q, int h_kv, int d, int C,
                                  int causal, int n_seqs, int jagged, int dtype);
 

@@ -43,6 +43,12 @@ def test_version_and_tile_rows():
 
 def test_workspace_sizes():
     assert F.ring_attn_workspace_bytes(8192, 8192, 32, 8, 128, 8, 1, 1, 0, F.BF16) == 0
+    # fp32 dense: a call of 1 query tile is split over its KV range -- the 4
+    # chunks of 128 keys cut into 4 parts of 32 each: 16 partial triplets of
+    # (d + 2) fp32 per row -- while 128 tiles or more need no workspace
+    assert F.ring_attn_workspace_bytes(128, 512, 1, 1, 64, 4, 0, 1, 0, F.F32) == \
+        16 * 128 * 64 * 4 + 2 * 16 * 128 * 4
+    assert F.ring_attn_workspace_bytes(2048, 2048, 8, 8, 64, 4, 1, 1, 0, F.F32) == 0
     n = F.ring_attn_workspace_bytes(1240379, 1240379, 4, 4, 128, 1, 1, 1152, 1, F.BF16)
     cap = 1240379 // 128 + 1152
     assert n >= 256 + 32 * cap

@@ -79,6 +79,23 @@ def test_prefill_f32_sweep(T, h_q, h_kv, d, causal, C):
     check(got, oracle.attention_ref(q, k, v, causal=causal), "f32", "f32 sweep")
 
 
+@pytest.mark.parametrize("T,h_q,causal,window", [(1024, 16, True, None), (128, 1, True, None),
+                                                 (128, 1, False, None), (1024, 16, True, 300),
+                                                 (96, 2, True, 40)])
+def test_prefill_f32_fused_and_split(T, h_q, causal, window):
+    """fp32 dense calls with 128 query tiles or more walk the ring in one
+    workgroup per tile; smaller ones are split over their KV range (a partial
+    per (tile, part), merged by lse_merge) and need a workspace.  Both paths
+    against the oracle."""
+    h_kv, d, C = 4 if h_q % 4 == 0 else 1, 64, 4
+    split = F.ring_attn_workspace_bytes(T, T, h_q, h_kv, d, C, int(causal), 1, 0, F.F32) > 0
+    assert split == (((T + 127) // 128) * h_q < 128)
+    q, k, v = _qkv(T, T, h_q, h_kv, d, "f32", T + h_q)
+    got = _run_ring(q, k, v, C=C, causal=causal, window=window)
+    check(got, oracle.attention_ref(q, k, v, causal=causal, window=window), "f32",
+          f"f32 {'split' if split else 'fused'} T={T} h={h_q}")
+
+
 JAGGED = [[1, 0, 130, 64, 257, 2, 33], [0, 0, 5], [300], [128, 129, 127, 1, 1]]
 
 
