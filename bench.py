@@ -56,6 +56,8 @@ def csrc_hash() -> str:
     h = hashlib.sha256()
     d = os.path.join(ROOT, "flash_attention_kv_amd", "csrc")
     for f in sorted(os.listdir(d)):
+        if not f.endswith((".hip", ".h", ".inc")):
+            continue      # caches and other non-source entries
         h.update(f.encode())
         h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]

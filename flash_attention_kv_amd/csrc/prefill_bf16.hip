@@ -35,8 +35,8 @@ int prefill_bf16_persistent_grid(int d, int qh) {
 hipError_t launch_prefill_bf16(const PrefillParams& p, int d, int qh, int grid, hipStream_t stream) {
   const bool jagged = p.sched != nullptr;
   switch (d) {
-    case 64: return jagged ? launch_qh<64, kWavesJagged>(p, qh, grid, stream) : launch_qh<64, kWavesDense>(p, qh, grid, stream);
-    case 128: return jagged ? launch_qh<128, kWavesJagged>(p, qh, grid, stream) : launch_qh<128, kWavesDense>(p, qh, grid, stream);
+    case 64: return jagged ? launch_qh<64, true>(p, qh, grid, stream) : launch_qh<64, false>(p, qh, grid, stream);
+    case 128: return jagged ? launch_qh<128, true>(p, qh, grid, stream) : launch_qh<128, false>(p, qh, grid, stream);
     case 256: return launch_prefill_bf16_d256(p, qh, grid, stream);
   }
   return hipErrorInvalidValue;

@@ -10,8 +10,8 @@
 namespace fakv {
 
 hipError_t launch_prefill_bf16_d256(const PrefillParams& p, int qh, int grid, hipStream_t stream) {
-  return p.sched != nullptr ? launch_qh<256, kWavesJagged>(p, qh, grid, stream)
-                            : launch_qh<256, kWavesDense>(p, qh, grid, stream);
+  return p.sched != nullptr ? launch_qh<256, true>(p, qh, grid, stream)
+                            : launch_qh<256, false>(p, qh, grid, stream);
 }
 
 int prefill_bf16_resident_d256(int qh) { return resident_qh<256>(qh); }

@@ -392,13 +392,24 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
   }
 }
 
-template <int D, int QH, int NW>
+// Dense batches run 4 waves per workgroup (two workgroups per CU); jagged
+// batches run 8 (one per CU): two query tiles' worth of rows share every K/V
+// tile brought into LDS -- the "grouping 2" of the Helion page's flattened
+// worklists -- which halves the tile loads per FLOP on the many short tiles
+// of a jagged batch (measured +3 % there, -3 % on the dense d = 256 batch).
+constexpr int kWavesDense = 4;
+constexpr int kWavesJagged = 8;
+
+// JAG instances run jagged batches only (persistent, p.sched set), the others
+// dense batches only; each instance holds just its own path, which keeps the
+// other path's registers out of its allocation.
+template <int D, int QH, int NW, bool JAG>
 __global__ __launch_bounds__(64 * NW, 8 / NW)
 void prefill_bf16_kernel(PrefillParams p) {
   constexpr int BQ = 32 * (NW / QH);
   __shared__ __attribute__((aligned(16))) char smem[4 * 16384];  // K0 V0 K1 V1
 
-  if (p.sched != nullptr) {
+  if constexpr (JAG) {
     // Jagged batch, persistent and statically scheduled.  Queue x holds the
     // entries (item * n_hg + head group) meant for XCD x -- workgroup L runs
     // on XCD L % 8 -- as whole (sequence, head group) units, longest first,
@@ -456,64 +467,57 @@ void prefill_bf16_kernel(PrefillParams p) {
       e0 = e1;
       e1 = entry_of(vn, slot_of(r + 2));
     }
-    return;
-  }
-
-  // Dense batch, one query tile per workgroup.  XCD-aware order: workgroups
-  // are dispatched round-robin over the 8 XCDs (workgroup L runs on XCD
-  // L % 8).  Group g of (sequence, head-group) pairs p = 8g .. 8g+7 places
-  // pair 8g + x on XCD x, so all query tiles of one pair -- which read the
-  // same K/V -- run on one XCD and share its L2; within a pair the longest
-  // causal tiles go first.
-  const int pairs = p.n_seqs * p.n_hg;
-  const int main_pairs = pairs & ~7;
-  const int L = blockIdx.x;
-  int pair, qr;
-  if (L < main_pairs * p.n_qtiles) {
-    const int slot = L >> 3;
-    const int pl = slot / p.n_qtiles;
-    qr = slot - pl * p.n_qtiles;
-    pair = pl * 8 + (L & 7);
   } else {
-    const int R = L - main_pairs * p.n_qtiles;
-    const int rp = pairs - main_pairs;
-    qr = R / rp;
-    pair = main_pairs + (R - qr * rp);
+    // Dense batch, one query tile per workgroup.  XCD-aware order: workgroups
+    // are dispatched round-robin over the 8 XCDs (workgroup L runs on XCD
+    // L % 8).  Group g of (sequence, head-group) pairs p = 8g .. 8g+7 places
+    // pair 8g + x on XCD x, so all query tiles of one pair -- which read the
+    // same K/V -- run on one XCD and share its L2; within a pair the longest
+    // causal tiles go first.
+    const int pairs = p.n_seqs * p.n_hg;
+    const int main_pairs = pairs & ~7;
+    const int L = blockIdx.x;
+    int pair, qr;
+    if (L < main_pairs * p.n_qtiles) {
+      const int slot = L >> 3;
+      const int pl = slot / p.n_qtiles;
+      qr = slot - pl * p.n_qtiles;
+      pair = pl * 8 + (L & 7);
+    } else {
+      const int R = L - main_pairs * p.n_qtiles;
+      const int rp = pairs - main_pairs;
+      qr = R / rp;
+      pair = main_pairs + (R - qr * rp);
+    }
+    const int qt = p.n_qtiles - 1 - qr;
+    const int seq = pair / p.n_hg;
+    ItemGeo g;
+    g.hg = pair - seq * p.n_hg;
+    g.seq_q0 = seq * p.T_q;
+    g.seq_k0 = seq * p.S_kv;
+    g.Lq = p.T_q;
+    g.Lk = p.S_kv;
+    g.q_lo = qt * BQ;
+    g.q_hi = min(g.q_lo + BQ, g.Lq);
+    g.jagged = 0;
+    prefill_item<D, QH, NW>(p, smem, g);
   }
-  const int qt = p.n_qtiles - 1 - qr;
-  const int seq = pair / p.n_hg;
-  ItemGeo g;
-  g.hg = pair - seq * p.n_hg;
-  g.seq_q0 = seq * p.T_q;
-  g.seq_k0 = seq * p.S_kv;
-  g.Lq = p.T_q;
-  g.Lk = p.S_kv;
-  g.q_lo = qt * BQ;
-  g.q_hi = min(g.q_lo + BQ, g.Lq);
-  g.jagged = 0;
-  prefill_item<D, QH, NW>(p, smem, g);
 }
 
-// Dense batches run 4 waves per workgroup (two workgroups per CU); jagged
-// batches run 8 (one per CU): two query tiles' worth of rows share every K/V
-// tile brought into LDS -- the "grouping 2" of the Helion page's flattened
-// worklists -- which halves the tile loads per FLOP on the many short tiles
-// of a jagged batch (measured +3 % there, -3 % on the dense d = 256 batch).
-constexpr int kWavesDense = 4;
-constexpr int kWavesJagged = 8;
-
-template <int D, int QH, int NW>
+template <int D, int QH, bool JAG>
 inline hipError_t launch_one(const PrefillParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, QH, NW>), dim3(grid), dim3(64 * NW), 0, stream, p);
+  constexpr int NW = JAG ? kWavesJagged : kWavesDense;
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, QH, NW, JAG>), dim3(grid), dim3(64 * NW), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, int NW>
+// JAG: the persistent instances of jagged batches (p.sched set), else the dense ones
+template <int D, bool JAG>
 inline hipError_t launch_qh(const PrefillParams& p, int qh, int grid, hipStream_t stream) {
   switch (qh) {
-    case 1: return launch_one<D, 1, NW>(p, grid, stream);
-    case 2: return launch_one<D, 2, NW>(p, grid, stream);
-    case 4: return launch_one<D, 4, NW>(p, grid, stream);
+    case 1: return launch_one<D, 1, JAG>(p, grid, stream);
+    case 2: return launch_one<D, 2, JAG>(p, grid, stream);
+    case 4: return launch_one<D, 4, JAG>(p, grid, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -521,7 +525,7 @@ inline hipError_t launch_qh(const PrefillParams& p, int qh, int grid, hipStream_
 template <int D, int QH>
 inline int resident_per_cu() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_bf16_kernel<D, QH, kWavesJagged>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_bf16_kernel<D, QH, kWavesJagged, true>,
                                                    64 * kWavesJagged, 0) != hipSuccess)
     n = 1;
   return n > 0 ? n : 1;
