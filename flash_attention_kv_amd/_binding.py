@@ -9,6 +9,7 @@ there is no fallback of any kind.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from typing import Optional, Tuple
 
@@ -76,15 +77,15 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 def _dev(*ts: torch.Tensor):
-    dev = ts[0].device
+    idx = ts[0].get_device()          # -1 for host tensors
     for t in ts:
-        if t.device.type != "cuda":
+        if not t.is_cuda:
             raise ValueError("tensors must be on a HIP device")
-        if t.device != dev:
+        if t.get_device() != idx:
             raise ValueError("tensors must be on the same device")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
-    return dev
+    return ts[0].device
 
 
 def _out_like(out: Optional[torch.Tensor], ref: torch.Tensor) -> torch.Tensor:
@@ -99,20 +100,35 @@ def _out_like(out: Optional[torch.Tensor], ref: torch.Tensor) -> torch.Tensor:
 
 
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # a plain int: the c_void_p argtypes convert it (None is NULL)
+    return None if t is None else t.data_ptr()
 
 
-def _stream(dev) -> ctypes.c_void_p:
-    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+# torch's current HIP stream of a device as a raw handle.  The raw-stream query
+# skips building a torch.cuda.Stream object per call (about 1.7 us on the
+# host); where this torch build lacks it, the public API gives the same handle.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(dev) -> int:
+    if _raw_stream is not None:
+        return _raw_stream(dev.index if dev.index is not None else torch.cuda.current_device())
+    return torch.cuda.current_stream(dev).cuda_stream
 
 
 def query_tile_rows(h_q: int, h_kv: int, d: int, dtype: int = BF16) -> int:
     return lib().fakv_query_tile_rows(h_q, h_kv, d, dtype)
 
 
+@functools.lru_cache(maxsize=256)
+def _ring_ws_bytes(T_q, S_kv, h_q, h_kv, d, C, causal, n_seqs, jagged, dtype) -> int:
+    return lib().ring_attn_workspace_bytes(T_q, S_kv, h_q, h_kv, d, C, causal, n_seqs, jagged, dtype)
+
+
 def ring_attn_workspace_bytes(T_q, S_kv, h_q, h_kv, d, C, causal, n_seqs, jagged, dtype) -> int:
-    return lib().ring_attn_workspace_bytes(T_q, S_kv, h_q, h_kv, d, C, int(causal), n_seqs,
-                                           int(jagged), dtype)
+    # a pure function of its integer arguments: cached per shape
+    return _ring_ws_bytes(int(T_q), int(S_kv), int(h_q), int(h_kv), int(d), int(C), int(causal),
+                          int(n_seqs), int(jagged), int(dtype))
 
 
 def splitkv_decode_workspace_bytes(B, h_q, d, n_chunks) -> int:
