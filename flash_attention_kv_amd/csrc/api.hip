@@ -85,7 +85,7 @@ size_t f32_split_bytes(int parts, size_t rows, int d) {
   return align256(n * d * 4) + 2 * align256(n * 4);
 }
 
-// Jagged-batch workspace: [header 256 B: n_items, queue info] [records]
+// Jagged-batch workspace: [header 256 B: n_items; queue lengths and pop counters from byte 64] [records]
 // and, for bf16, the per-XCD schedule arrays.
 struct JaggedLayout {
   size_t items, nat2canon, ntprefix, seq_of_rank, sched, total;

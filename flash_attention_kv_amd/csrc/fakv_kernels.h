@@ -28,7 +28,7 @@ struct PrefillParams {
   const int32_t* n_items;  // device count of records
   const int32_t* sched;    // bf16 jagged: 8 per-XCD queues of item * n_hg + head group
   int sched_stride;        // entries reserved per queue
-  int32_t* qinfo;          // queue lengths [0..7]
+  int32_t* qinfo;          // queue lengths [0..7]; the queues' pop counters at [16 + 4 q]
   int n_qtiles;            // dense: query tiles per sequence
   int n_hg;                // workgroups per query tile = h_q / heads per workgroup
   float scale;             // 1 / sqrt(d)
@@ -78,7 +78,7 @@ hipError_t launch_worklist(const int32_t* seq_offsets, int n_seqs, int total, in
 
 // Workspace carve-up of the per-XCD schedule built after the worklist.
 struct SchedBufs {
-  int32_t* qinfo;          // 8 ints: queue lengths
+  int32_t* qinfo;          // queue lengths [0..7]; pop counters at [16 + 4 q] (the schedule kernel zeroes them)
   int32_t* nat2canon;      // capacity ints: (seq, tile) in natural order -> record index
   int32_t* ntprefix;       // n_seqs + 1 ints: prefix sums of tiles per sequence
   int32_t* seq_of_rank;    // n_seqs ints: sequences sorted by tile count, descending

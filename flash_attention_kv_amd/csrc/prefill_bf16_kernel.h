@@ -62,10 +62,16 @@ struct ItemGeo {
   int jagged;           // chunk width rounds up (jagged) or divides exactly (dense)
 };
 
+struct NoHook {
+  __device__ void operator()() const {}
+};
+
 // One work item, start to finish: Q rows into registers, the KV walk, the
-// epilogue.  The workgroup's LDS is free on entry and on exit.
-template <int D, int QH, int NW>
-__device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem, const ItemGeo& g) {
+// epilogue.  The workgroup's LDS is free on entry and on exit.  last_step()
+// runs in every wave during the item's last tile, before its final barrier.
+template <int D, int QH, int NW, class Hook = NoHook>
+__device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem, const ItemGeo& g,
+                                             Hook last_step = Hook{}) {
   constexpr int BK = TileK<D>::BK;
   constexpr int WPH = NW / QH;         // waves per query head
   constexpr int BQ = 32 * WPH;         // query rows per tile
@@ -347,11 +353,13 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
         });
       });
     }
+    if (!nxt.valid) last_step();
     wait_dma_and_sync();
     walk = nxt;
   };
 
   if (walk.valid) issue_tile(walk.kt, 0);
+  else last_step();                          // no tile: the hook still runs once
   wait_dma_and_sync();
   while (walk.valid) {
     step(std::integral_constant<int, 0>{});
@@ -410,62 +418,122 @@ void prefill_bf16_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) char smem[4 * 16384];  // K0 V0 K1 V1
 
   if constexpr (JAG) {
-    // Jagged batch, persistent and statically scheduled.  Queue x holds the
+    // Jagged batch, persistent, drained dynamically.  Queue x holds the
     // entries (item * n_hg + head group) meant for XCD x -- workgroup L runs
     // on XCD L % 8 -- as whole (sequence, head group) units, longest first,
     // so the query tiles that share one sequence's K/V run on one XCD and
-    // hit its L2.  The grid is a multiple of 8; the G / 8 workgroups of XCD x
-    // deal the entries of queue x among themselves in zigzag rounds.  No
-    // atomics: every workgroup knows its entries.  The next item's record
-    // and the entry after it come in with one vector load issued before the
-    // current item runs -- lanes 0..3 fetch record words 2, 3, 4 and 6, lane
-    // 4 the queue entry, so the value is not uniform and stays in a vector
-    // register until it is read after the item: the chain entry -> record
-    // never stalls an item's start.
-    const int x = blockIdx.x & 7;
-    const int nj = gridDim.x >> 3;
-    const int len = p.qinfo[x];
-    const int32_t* q = p.sched + (size_t)x * p.sched_stride;
+    // hit its L2 (the worklist of the Helion page's "Flattened worklists",
+    // dealt per XCD).  The workgroups of XCD x take queue x's entries in order
+    // through an atomic counter, so each one takes the longest entry left
+    // whenever it finishes an item, and a workgroup whose queue runs dry
+    // takes entries from the next queues: the XCDs finish together instead of
+    // each workgroup running a fixed share.
+    //
+    // Only wave 0 touches the queues, three items ahead, so no request is
+    // waited for where it was issued: when item r starts it reads the record
+    // of item r + 1 (its entry came in during item r - 1), reads the entry of
+    // item r + 2 (its counter came in during item r - 1) and pops the counter
+    // of item r + 3.  During item r's last tile -- before that tile's final
+    // barrier -- it publishes item r + 1's record in LDS, where every wave
+    // reads it once item r is done.
+    __shared__ int mbox[2][8];                      // s0, L, lo, hi, head group, valid
     const int lane = threadIdx.x & 63;
-    // Round r covers slots [r nj, (r + 1) nj); workgroup j takes slot j of
-    // even rounds and slot nj - 1 - j of odd ones, so a workgroup that drew a
-    // long tile of a unit draws a short one next.
-    const int j = blockIdx.x >> 3;
-    auto slot_of = [&](int r) { return r * nj + ((r & 1) ? nj - 1 - j : j); };
-    // record of the item of entry e (item 0 when e < 0, read and ignored) and
-    // the entry at slot (entry 0 when slot >= len, read and ignored)
-    auto fetch = [&](int e, int slot) {
-      const int32_t* it = p.items + 8 * (size_t)(e >= 0 ? e / p.n_hg : 0);
-      const int li = lane & 7;
-      const int32_t* a = li == 0 ? it + 2 : li == 1 ? it + 3 : li == 2 ? it + 4 : li == 3 ? it + 6
-                                                                        : q + (slot < len ? slot : 0);
-      return *a;
+    const bool w0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0;
+    int32_t* cnt = p.qinfo + 16;                    // pop counter of queue q at cnt[4 q], zeroed by the scheduler
+    auto qlen = [&](int qq) { return p.qinfo[qq]; };
+    auto qent = [&](int qq, int slot) { return p.sched + (size_t)qq * p.sched_stride + slot; };
+    int pq = blockIdx.x & 7;                        // queue being drained
+    unsigned dry = 0;                               // queues found empty (bit mask)
+    // Lane 0 pops queue pq; the old count lands in a vector register, read later.
+    auto pop = [&]() {
+      int v = 0;
+      if (lane == 0) v = atomicAdd(cnt + 4 * pq, 1);
+      return v;
     };
-    struct Rec { int s0, L, lo, hi; };
-    auto rec_of = [&](int v) {
-      return Rec{__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 1),
-                 __builtin_amdgcn_readlane(v, 2), __builtin_amdgcn_readlane(v, 3)};
+    // A popped slot of queue pq, or (when pq has run dry) a slot popped from
+    // the next queue not yet found empty, at once; -1 once every queue is empty.
+    auto resolve = [&](int s) {
+      while (s >= qlen(pq)) {
+        dry |= 1u << pq;
+        if (dry == 0xFFu) return -1;
+        int k = 1;
+        while (dry & (1u << ((pq + k) & 7))) ++k;
+        pq = (pq + k) & 7;
+        s = __builtin_amdgcn_readfirstlane(pop());
+      }
+      return s;
     };
-    auto entry_of = [&](int v, int slot) { return slot < len ? __builtin_amdgcn_readlane(v, 4) : -1; };
-    if (slot_of(0) >= len) return;
-    int e0 = q[slot_of(0)];
-    const int v0 = fetch(e0, slot_of(1));
-    Rec rc = rec_of(v0);
-    int e1 = entry_of(v0, slot_of(1));
+    // The entry at slot s of queue pq in lane 0; the other lanes read slot 0,
+    // so the address is not uniform and the value stays in a vector register.
+    auto entry_load = [&](int s) { return *qent(pq, lane == 0 ? s : 0); };
+    // Lanes 0..3: words 2, 3, 4, 6 of the record of entry e's item.
+    auto rec_load = [&](int e) {
+      const int32_t* it = p.items + 8 * (size_t)(e / p.n_hg);
+      const int li = lane & 3;
+      return it[li == 0 ? 2 : li == 1 ? 3 : li == 2 ? 4 : 6];
+    };
+    auto publish_rec = [&](int* mo, bool ok, int rv, int e) {
+      if (lane == 0) {
+        mo[0] = ok ? __builtin_amdgcn_readlane(rv, 0) : 0;
+        mo[1] = ok ? __builtin_amdgcn_readlane(rv, 1) : 0;
+        mo[2] = ok ? __builtin_amdgcn_readlane(rv, 2) : 0;
+        mo[3] = ok ? __builtin_amdgcn_readlane(rv, 3) : 0;
+        mo[4] = ok ? e % p.n_hg : 0;
+        mo[5] = ok;
+      }
+    };
+    // wave 0's pipeline: ev = entry of the next item but one (lane 0), pv = a
+    // pending pop for the item after that
+    int ev = 0, pv = 0;
+    bool ev_ok = false, pv_ok = false;
+    if (w0) {                                       // item 0 at once, item 1's entry and item 2's pop in flight
+      const int s0 = resolve(__builtin_amdgcn_readfirstlane(pop()));
+      const int e0 = s0 >= 0 ? __builtin_amdgcn_readlane(entry_load(s0), 0) : 0;
+      publish_rec(mbox[0], s0 >= 0, s0 >= 0 ? rec_load(e0) : 0, e0);
+      if (s0 >= 0) {
+        const int s1 = resolve(__builtin_amdgcn_readfirstlane(pop()));
+        if (s1 >= 0) {
+          ev = entry_load(s1);
+          ev_ok = true;
+          pv = pop();
+          pv_ok = true;
+        }
+      }
+    }
+    __syncthreads();
     for (int r = 0;; ++r) {
-      const int vn = fetch(e1, slot_of(r + 2));   // record of item r + 1, entry of item r + 2
+      const int* mb = mbox[r & 1];
+      if (!mb[5]) break;
       ItemGeo g;
-      g.seq_q0 = g.seq_k0 = rc.s0;
-      g.Lq = g.Lk = rc.L;
-      g.q_lo = rc.lo - rc.s0;
-      g.q_hi = rc.hi - rc.s0;
-      g.hg = e0 % p.n_hg;
+      g.seq_q0 = g.seq_k0 = mb[0];
+      g.Lq = g.Lk = mb[1];
+      g.q_lo = mb[2] - mb[0];
+      g.q_hi = mb[3] - mb[0];
+      g.hg = mb[4];
       g.jagged = 1;
-      prefill_item<D, QH, NW>(p, smem, g);
-      if (e1 < 0) break;
-      rc = rec_of(vn);
-      e0 = e1;
-      e1 = entry_of(vn, slot_of(r + 2));
+      int rv = 0, e1 = 0;
+      bool ok1 = false;
+      if (w0) {
+        ok1 = ev_ok;                                // item r + 1: its record
+        if (ok1) {
+          e1 = __builtin_amdgcn_readlane(ev, 0);
+          rv = rec_load(e1);
+        }
+        ev_ok = false;                              // item r + 2: its entry, then item r + 3's pop
+        if (pv_ok) {
+          const int s2 = resolve(__builtin_amdgcn_readfirstlane(pv));
+          if (s2 >= 0) {
+            ev = entry_load(s2);
+            ev_ok = true;
+            pv = pop();
+          }
+        }
+        pv_ok = ev_ok;
+      }
+      int* mo = mbox[(r + 1) & 1];
+      prefill_item<D, QH, NW>(p, smem, g, [&]() {
+        if (w0) publish_rec(mo, ok1, rv, e1);
+      });
     }
   } else {
     // Dense batch, one query tile per workgroup.  XCD-aware order: workgroups

@@ -163,6 +163,7 @@ void schedule_kernel(const int32_t* __restrict__ off, int n_seqs, int BQ, const 
   const int n_items = *n_items_p;
   if (n_items == 0) {          // empty batch or rejected offsets
     if (tid < 16) sb.qinfo[tid] = 0;
+    if (tid < 8) sb.qinfo[16 + 4 * tid] = 0;        // the queues' pop counters
     return;
   }
   // (offsets are a valid prefix array here: worklist_kernel checked every
@@ -263,6 +264,7 @@ void schedule_kernel(const int32_t* __restrict__ off, int n_seqs, int BQ, const 
     __syncthreads();
   }
   if (tid < 8) sb.qinfo[tid] = s_carry[tid];
+  if (tid < 8) sb.qinfo[16 + 4 * tid] = 0;          // the queues' pop counters
 }
 
 hipError_t launch_schedule(const int32_t* seq_offsets, int n_seqs, int BQ, const int32_t* items,
