@@ -4,9 +4,13 @@
 // masks, jagged items, triplet modes), evaluated in fp32 end to end on the
 // fp32 MFMA (v_mfma_f32_32x32x2f32: products and sums in fp32, no operand
 // rounding).  With a contraction depth of 2 per instruction each lane holds a
-// single k-value per operand, so V needs no transposition: for the value
+// single k-value per operand.  In S^T = K Q^T k-step s pairs head dims s and
+// s + D/2 (the lane's half picks which), so a lane's Q values and its slice
+// of a K row are contiguous: Q arrives by 16-byte loads and K by 16-byte LDS
+// reads, issued ahead of the MFMAs.  V needs no transposition: for the value
 // product O^T += V^T P^T the lane's own P register is the B operand and V is
-// read row-major.  One workgroup = 4 waves = 128 query rows of one head.
+// read row-major, one 32-dim block ahead of its MFMAs (the first block while
+// the softmax runs).  One workgroup = 4 waves = 128 query rows of one head.
 //
 // Split-KV mode (kv_parts = P > 0, dense batches): the ring's C chunks are cut
 // into P equal parts (P a multiple of C, so every part lies inside one ring
@@ -26,7 +30,7 @@ void prefill_f32_kernel(PrefillParams p) {
   constexpr int BK = 32;               // keys per tile (one MFMA block)
   constexpr int BQ = 128;
   constexpr int DB = D / 32;
-  constexpr int KST = D + 2;           // LDS row stride (floats) of K: conflict-free column reads
+  constexpr int KST = D + 4;           // LDS row stride (floats) of K: 16-byte rows, 4-bank skew
   constexpr int VST = D + 8;           // LDS row stride (floats) of V
   constexpr int KBYTES = BK * KST * 4;
   constexpr int VBYTES = BK * VST * 4;
@@ -99,10 +103,23 @@ void prefill_f32_kernel(PrefillParams p) {
   const bool qvalid = qi < q_hi;
   const size_t qrow = (size_t)(seq_q0 + qi) * p.h_q + head;
 
-  // Q^T as B operands: k-step s covers dims 2s, 2s+1; this lane holds dim 2s + half.
+  // Q^T as B operands: k-step s covers dims s and s + D/2; this lane holds
+  // dim s + (D/2) half, i.e. D/2 contiguous floats.
   float qreg[D / 2];
+  {
+    f32x4 qv[D / 8];
 #pragma unroll
-  for (int s = 0; s < D / 2; ++s) qreg[s] = qvalid ? Q[qrow * D + 2 * s + half] : 0.f;
+    for (int i = 0; i < D / 8; ++i) qv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (qvalid) {
+      const float* qp = Q + qrow * D + (D / 2) * half;
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) qv[i] = *reinterpret_cast<const f32x4*>(qp + 4 * i);
+    }
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qreg[4 * i + j] = qv[i][j];
+  }
 
   f32x16 oacc[DB];
 #pragma unroll
@@ -142,9 +159,7 @@ void prefill_f32_kernel(PrefillParams p) {
     for (int i = 0; i < CH; ++i) {
       const int id = tid + 256 * i;
       const int r = id / NCH, c = id % NCH;
-      f32x2 lo = {kst[i][0], kst[i][1]}, hi = {kst[i][2], kst[i][3]};
-      *reinterpret_cast<f32x2*>(kl + r * KST + 4 * c) = lo;
-      *reinterpret_cast<f32x2*>(kl + r * KST + 4 * c + 2) = hi;
+      *reinterpret_cast<f32x4*>(kl + r * KST + 4 * c) = kst[i];
       *reinterpret_cast<f32x4*>(vl + r * VST + 4 * c) = vst[i];
     }
   };
@@ -165,9 +180,32 @@ void prefill_f32_kernel(PrefillParams p) {
     if (!skip) {
       const float* kl = reinterpret_cast<const float*>(smem + buf * (KBYTES + VBYTES));
       const float* vl = reinterpret_cast<const float*>(smem + buf * (KBYTES + VBYTES) + KBYTES);
+      // S^T = K Q^T: the lane's K slice in 16-byte reads, KC of them (4
+      // k-steps each) in flight before their MFMAs
+      constexpr int KG = D / 8;
+      constexpr int KC = KG < 16 ? KG : 16;
+      const float* krow = kl + col * KST + (D / 2) * half;
       f32x16 sacc = f32x16{};
 #pragma unroll
-      for (int s = 0; s < D / 2; ++s) sacc = mfma32x32x2f32(kl[col * KST + 2 * s + half], qreg[s], sacc);
+      for (int c0 = 0; c0 < KG; c0 += KC) {
+        f32x4 kv[KC];
+#pragma unroll
+        for (int g = 0; g < KC; ++g) kv[g] = *reinterpret_cast<const f32x4*>(krow + 4 * (c0 + g));
+#pragma unroll
+        for (int g = 0; g < KC; ++g)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sacc = mfma32x32x2f32(kv[g][j], qreg[4 * (c0 + g) + j], sacc);
+      }
+      // V operands of dim block 0, in flight while the softmax runs
+      float vv[2][16];
+      auto read_v = [&](int b, float* dst) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 8 * (r >> 2) + 4 * half + (r & 3);
+          dst[r] = vl[key * VST + 32 * b + col];
+        }
+      };
+      read_v(0, vv[0]);
       const bool need_mask = (kt + BK > end) || (p.causal && (kt + BK - 1 > qw_lo + delta)) ||
                              (win > 0 && kt < qw_hi - 1 + delta - win + 1);
       if (need_mask) {
@@ -197,12 +235,10 @@ void prefill_f32_kernel(PrefillParams p) {
       m_run = m_new;
 #pragma unroll
       for (int b = 0; b < DB; ++b) {
+        if (b + 1 < DB) read_v(b + 1, vv[(b + 1) & 1]);
         f32x16 acc = oacc[b] * alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 8 * (r >> 2) + 4 * half + (r & 3);
-          acc = mfma32x32x2f32(vl[key * VST + 32 * b + col], sacc[r], acc);
-        }
+        for (int r = 0; r < 16; ++r) acc = mfma32x32x2f32(vv[b & 1][r], sacc[r], acc);
         oacc[b] = acc;
       }
     }
@@ -249,7 +285,7 @@ void prefill_f32_kernel(PrefillParams p) {
 
 template <int D>
 static hipError_t launch_f32(const PrefillParams& p, int grid, hipStream_t stream) {
-  constexpr int smem = 2 * (32 * (D + 2) * 4 + 32 * (D + 8) * 4);
+  constexpr int smem = 2 * (32 * (D + 4) * 4 + 32 * (D + 8) * 4);
   static std::atomic<unsigned> lds_done{0};
   auto kern = prefill_f32_kernel<D>;
   hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), smem, lds_done);
