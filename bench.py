@@ -52,12 +52,32 @@ BF16_FLOP_PER_CLK_CU = 4096    # dense bf16 MFMA FLOP per clock per CU
 METRIC = "useful causal TFLOP/s (prefill) and HBM GB/s (split-KV decode), % of roofline"
 
 
-def csrc_hash() -> str:
+# Sources each measured kernel is built from: the shared headers and the
+# launch code, plus its own translation units.  A counter entry stays valid
+# while these files are unchanged, whatever else changes in csrc/.
+_SHARED_SOURCES = ("fakv_device.h", "fakv_kernels.h", "api.hip")
+_FAMILY_SOURCES = {
+    "prefill_bf16": ("prefill_bf16_kernel.h", "prefill_bf16.hip", "prefill_bf16_d256.hip", "worklist.hip"),
+    "decode": ("decode.hip", "merge.hip"),
+}
+_WORKLOAD_FAMILY = {"gqa_ring": "prefill_bf16", "dense_causal": "prefill_bf16", "jagged": "prefill_bf16",
+                    "gqa_swa": "prefill_bf16", "jagged_sched": "prefill_bf16", "jagged_worklist": "prefill_bf16",
+                    "decode": "decode", "decode_merge": "decode"}
+
+
+def csrc_hash(workload: str = None) -> str:
+    """Hash of the kernel sources: all of csrc/ (workload None), or the files
+    the given workload's kernels are built from."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "flash_attention_kv_amd", "csrc")
-    for f in sorted(os.listdir(d)):
-        if not f.endswith((".hip", ".h", ".inc")):
-            continue      # caches and other non-source entries
+    if workload is None:
+        names = [f for f in sorted(os.listdir(d)) if f.endswith((".hip", ".h", ".inc"))]
+    else:
+        fam = _WORKLOAD_FAMILY.get(workload)
+        if fam is None:
+            return ""
+        names = sorted(_SHARED_SOURCES + _FAMILY_SOURCES[fam])
+    for f in names:
         h.update(f.encode())
         h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
@@ -66,7 +86,7 @@ def csrc_hash() -> str:
 def load_counter(workload: str, key: str):
     """A per-launch figure of the dominant kernel from the committed rocprofv3
     counter summary (profiles/counters.json), if it was measured on the
-    current kernel sources, else None."""
+    current sources of that kernel, else None."""
     p = os.path.join(ROOT, "profiles", "counters.json")
     if not os.path.exists(p):
         return None
@@ -75,7 +95,7 @@ def load_counter(workload: str, key: str):
     except ValueError:
         return None
     ent = data.get(workload)
-    if not ent or ent.get("csrc_hash") != csrc_hash():
+    if not ent or ent.get("csrc_hash") != csrc_hash(workload):
         return None
     return ent.get(key)
 

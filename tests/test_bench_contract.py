@@ -25,7 +25,7 @@ def test_traffic_follows_the_kernel_sources(tmp_path, monkeypatch):
         "gqa_ring": {"csrc_hash": "aaaa", "bytes_per_launch": 123},
         "decode": {"csrc_hash": "bbbb", "bytes_per_launch": 456}}))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    monkeypatch.setattr(bench, "csrc_hash", lambda: "aaaa")
+    monkeypatch.setattr(bench, "csrc_hash", lambda workload=None: "aaaa")
     assert bench.load_traffic("gqa_ring") == 123
     assert bench.load_traffic("decode") is None          # taken on other sources
     assert bench.load_traffic("jagged") is None          # never measured
@@ -36,3 +36,16 @@ def test_source_hash_covers_every_kernel_file():
     assert len(h) == 16 and h == bench.csrc_hash()
     srcs = sorted(os.listdir(os.path.join(ROOT, "flash_attention_kv_amd", "csrc")))
     assert any(s.endswith(".hip") for s in srcs) and "fakv_device.h" in srcs
+
+
+def test_counter_hash_follows_only_that_kernels_sources():
+    d = os.path.join(ROOT, "flash_attention_kv_amd", "csrc")
+    srcs = set(os.listdir(d))
+    for w, fam in bench._WORKLOAD_FAMILY.items():
+        files = bench._SHARED_SOURCES + bench._FAMILY_SOURCES[fam]
+        assert set(files) <= srcs, w
+        assert len(bench.csrc_hash(w)) == 16
+    # the fp32 prefill is no part of the bf16 or decode counter entries
+    assert all("prefill_f32.hip" not in f for f in bench._FAMILY_SOURCES.values())
+    assert bench.csrc_hash("gqa_ring") == bench.csrc_hash("jagged") != bench.csrc_hash("decode")
+    assert bench.csrc_hash("ring_tiny") == ""
