@@ -62,16 +62,31 @@ struct ItemGeo {
   int jagged;           // chunk width rounds up (jagged) or divides exactly (dense)
 };
 
-struct NoHook {
-  __device__ void operator()() const {}
+struct NoStepHook {
+  __device__ void operator()(int, bool) const {}
+};
+struct NoNextItem {
+  __device__ bool operator()(ItemGeo&) const { return false; }
 };
 
 // One work item, start to finish: Q rows into registers, the KV walk, the
-// epilogue.  The workgroup's LDS is free on entry and on exit.  last_step()
-// runs in every wave during the item's last tile, before its final barrier.
-template <int D, int QH, int NW, class Hook = NoHook>
-__device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem, const ItemGeo& g,
-                                             Hook last_step = Hook{}) {
+// epilogue.  The workgroup's LDS is free on entry and on exit.
+// on_step(i, last) runs in every wave during tile i of the walk (last: the
+// item's last tile), before that tile's final barrier; an item without tiles
+// still calls it once, as (0, true).
+// EARLY (persistent jagged workgroups, d <= 128): a wave that no later tile of
+// the walk concerns -- one ring chunk, causal, pruned, so key tiles come in
+// increasing order and a tile past the wave's last row ends its share --
+// writes its output at once and, from the third tile on (the next item's
+// record is published by the end of the second), copies the Q rows it will
+// have in next_item()'s geometry HBM -> LDS into its own d/16 KB of qstage,
+// setting q_ready: the next item then reads them from LDS.  Those waves sit
+// out the item's last diagonal tiles anyway, so the next item waits on fewer
+// loads and the output stores overlap the remaining tiles.
+template <int D, int QH, int NW, bool EARLY = false, class StepHook = NoStepHook, class NextItem = NoNextItem>
+__device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem, const ItemGeo& g, bool& q_ready,
+                                             StepHook on_step = StepHook{}, NextItem next_item = NextItem{},
+                                             char* qstage = nullptr) {
   constexpr int BK = TileK<D>::BK;
   constexpr int WPH = NW / QH;         // waves per query head
   constexpr int BQ = 32 * WPH;         // query rows per tile
@@ -83,6 +98,7 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
   constexpr int NCH = D / 8;           // 16-byte chunks per key row
   constexpr int NI = TILE / 16 / (64 * NW);  // DMA instructions per thread per tensor
   static_assert(TILE == 16384 && NI * 64 * NW * 16 == TILE, "tile geometry");
+  static_assert(!EARLY || D <= 128, "early hand-over needs the LDS of d <= 128");
 
 
   const int tid = threadIdx.x;
@@ -120,16 +136,45 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
   const bool qvalid = qi < q_hi;
   const size_t qrow = (size_t)(seq_q0 + qi) * p.h_q + head;
 
+  // this wave's Q rows of item gg, into registers
   bf16x8 qreg[DS];
-  {
-    const uint16_t* qp = p.q + qrow * D + 8 * half;
+  auto load_q = [&](const ItemGeo& gg) {
+    const int qi_g = gg.q_lo + 32 * qsub + col;
+    const bool valid_g = qi_g < gg.q_hi;
+    const size_t row_g = (size_t)(gg.seq_q0 + qi_g) * p.h_q + gg.hg * QH + hl;
+    const uint16_t* qp = p.q + row_g * D + 8 * half;
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (qvalid) x = *reinterpret_cast<const u32x4*>(qp + 16 * s);
+      if (valid_g) x = *reinterpret_cast<const u32x4*>(qp + 16 * s);
       qreg[s] = __builtin_bit_cast(bf16x8, x);
     }
+  };
+  // ... or HBM -> LDS, at this wave's DS KB of qstage (lane l's 16 bytes of
+  // k-step s at 1024 s + 16 l, the register layout); rows past the tile read 0
+  auto stage_q = [&](const ItemGeo& gg) {
+    const int r0 = gg.q_lo + 32 * qsub;
+    const int nr = min(32, gg.q_hi - r0);
+    const unsigned rstride = (unsigned)p.h_q * D * 2;
+    const unsigned ext = nr > 0 ? (unsigned)(nr - 1) * rstride + D * 2 : 0u;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(p.q + ((size_t)(gg.seq_q0 + r0) * p.h_q + gg.hg * QH + hl) * D, ext);
+    const unsigned vo = (unsigned)col * rstride + 16u * half;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) dma16(rs, vo + 32u * s, qstage + wave * (DS * 1024) + 1024 * s);
+  };
+  if constexpr (EARLY) {
+    if (q_ready) {
+      const char* src = qstage + wave * (DS * 1024) + 16 * lane;
+#pragma unroll
+      for (int s = 0; s < DS; ++s) qreg[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + 1024 * s));
+    } else {
+      load_q(g);
+    }
+  } else {
+    load_q(g);
   }
+  q_ready = false;
 
   f32x16 oacc[DB];
 #pragma unroll
@@ -210,6 +255,43 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
   const float scale = p.scale;
   const float scale_log2 = p.scale_log2;
 
+  // ---- epilogue: O / l in bf16, or the fp32 triplet ------------------------
+  auto epilogue = [&]() {
+    float l_tot = halves_sum(l_run);
+    if (!qvalid) return;
+    if (p.mode == 0) {
+      const float inv = 1.f / l_tot;
+      uint16_t* op = p.o + qrow * D + 4 * half;
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          u32x2 x = {pack_bf16x2(oacc[b][4 * g] * inv, oacc[b][4 * g + 1] * inv),
+                     pack_bf16x2(oacc[b][4 * g + 2] * inv, oacc[b][4 * g + 3] * inv)};
+          *reinterpret_cast<u32x2*>(op + 32 * b + 8 * g) = x;
+        }
+    } else {
+      // exported triplets are relative to the true row max
+      const float f = (m_true == neg_inf()) ? 1.f : fast_exp2((m_sh - m_true) * kLog2e);
+      l_tot *= f;
+      if (half == 0) {
+        p.m_st[qrow] = m_true;
+        p.l_st[qrow] = l_tot;
+      }
+      float* os = p.o_st + qrow * D + 4 * half;
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 x = {oacc[b][4 * g] * f, oacc[b][4 * g + 1] * f, oacc[b][4 * g + 2] * f, oacc[b][4 * g + 3] * f};
+          *reinterpret_cast<f32x4*>(os + 32 * b + 8 * g) = x;
+        }
+    }
+  };
+  bool epi_done = false;
+  const bool early_ok = EARLY && p.C == 1 && p.causal && p.prune;
+  int sidx = 0;
+
   // One tile of the walk on LDS buffer BUF (a compile-time constant, so LDS
   // addresses fold into immediates): prefetch the next tile into the other
   // buffer, compute this one, then wait for the prefetch and synchronise.
@@ -220,6 +302,21 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
     KvWalk nxt = walk;
     nxt.next();
     if (nxt.valid) issue_tile(nxt.kt, BUF ^ 1);
+    if constexpr (EARLY) {
+      if (early_ok && (!wave_active || kt > qw_hi - 1 + delta)) {   // no tile from here on is this wave's
+        if (!epi_done) {
+          epilogue();
+          epi_done = true;
+        }
+        if constexpr (EARLY) {
+          ItemGeo ng;
+          if (!q_ready && sidx >= 2 && next_item(ng)) {
+            stage_q(ng);
+            q_ready = true;
+          }
+        }
+      }
+    }
 
     const bool skip = !wave_active || (p.causal && p.prune && kt > qw_hi - 1 + delta) ||
                       (win > 0 && p.prune && kt + BK - 1 < qw_lo + delta - win + 1);
@@ -353,13 +450,14 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
         });
       });
     }
-    if (!nxt.valid) last_step();
+    on_step(sidx, !nxt.valid);
+    ++sidx;
     wait_dma_and_sync();
     walk = nxt;
   };
 
   if (walk.valid) issue_tile(walk.kt, 0);
-  else last_step();                          // no tile: the hook still runs once
+  else on_step(0, true);                     // no tile: the hook still runs once
   wait_dma_and_sync();
   while (walk.valid) {
     step(std::integral_constant<int, 0>{});
@@ -367,37 +465,7 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
     step(std::integral_constant<int, 1>{});
   }
 
-  // ---- epilogue -------------------------------------------------------------
-  float l_tot = halves_sum(l_run);
-  if (!qvalid) return;
-  if (p.mode == 0) {
-    const float inv = 1.f / l_tot;
-    uint16_t* op = p.o + qrow * D + 4 * half;
-#pragma unroll
-    for (int b = 0; b < DB; ++b)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 x = {pack_bf16x2(oacc[b][4 * g] * inv, oacc[b][4 * g + 1] * inv),
-                   pack_bf16x2(oacc[b][4 * g + 2] * inv, oacc[b][4 * g + 3] * inv)};
-        *reinterpret_cast<u32x2*>(op + 32 * b + 8 * g) = x;
-      }
-  } else {
-    // exported triplets are relative to the true row max
-    const float f = (m_true == neg_inf()) ? 1.f : fast_exp2((m_sh - m_true) * kLog2e);
-    l_tot *= f;
-    if (half == 0) {
-      p.m_st[qrow] = m_true;
-      p.l_st[qrow] = l_tot;
-    }
-    float* os = p.o_st + qrow * D + 4 * half;
-#pragma unroll
-    for (int b = 0; b < DB; ++b)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 x = {oacc[b][4 * g] * f, oacc[b][4 * g + 1] * f, oacc[b][4 * g + 2] * f, oacc[b][4 * g + 3] * f};
-        *reinterpret_cast<f32x4*>(os + 32 * b + 8 * g) = x;
-      }
-  }
+  if (!epi_done) epilogue();
 }
 
 // Dense batches run 4 waves per workgroup (two workgroups per CU); jagged
@@ -433,10 +501,11 @@ void prefill_bf16_kernel(PrefillParams p) {
     // waited for where it was issued: when item r starts it reads the record
     // of item r + 1 (its entry came in during item r - 1), reads the entry of
     // item r + 2 (its counter came in during item r - 1) and pops the counter
-    // of item r + 3.  During item r's last tile -- before that tile's final
-    // barrier -- it publishes item r + 1's record in LDS, where every wave
-    // reads it once item r is done.
-    __shared__ int mbox[2][8];                      // s0, L, lo, hi, head group, valid
+    // of item r + 3.  During item r's second tile (its only one, if so) --
+    // before that tile's final barrier -- it publishes item r + 1's record in
+    // LDS: waves done with item r early load their next Q rows from it, and
+    // every wave reads it once item r is done.
+    __shared__ int mbox[2][8];                      // s0, L, lo, hi, head group, valid, item number
     const int lane = threadIdx.x & 63;
     const bool w0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0;
     int32_t* cnt = p.qinfo + 16;                    // pop counter of queue q at cnt[4 q], zeroed by the scheduler
@@ -472,7 +541,7 @@ void prefill_bf16_kernel(PrefillParams p) {
       const int li = lane & 3;
       return it[li == 0 ? 2 : li == 1 ? 3 : li == 2 ? 4 : 6];
     };
-    auto publish_rec = [&](int* mo, bool ok, int rv, int e) {
+    auto publish_rec = [&](int* mo, bool ok, int rv, int e, int item) {
       if (lane == 0) {
         mo[0] = ok ? __builtin_amdgcn_readlane(rv, 0) : 0;
         mo[1] = ok ? __builtin_amdgcn_readlane(rv, 1) : 0;
@@ -480,7 +549,16 @@ void prefill_bf16_kernel(PrefillParams p) {
         mo[3] = ok ? __builtin_amdgcn_readlane(rv, 3) : 0;
         mo[4] = ok ? e % p.n_hg : 0;
         mo[5] = ok;
+        mo[6] = item;
       }
+    };
+    auto read_geo = [&](const int* mb, ItemGeo& g) {
+      g.seq_q0 = g.seq_k0 = mb[0];
+      g.Lq = g.Lk = mb[1];
+      g.q_lo = mb[2] - mb[0];
+      g.q_hi = mb[3] - mb[0];
+      g.hg = mb[4];
+      g.jagged = 1;
     };
     // wave 0's pipeline: ev = entry of the next item but one (lane 0), pv = a
     // pending pop for the item after that
@@ -489,7 +567,8 @@ void prefill_bf16_kernel(PrefillParams p) {
     if (w0) {                                       // item 0 at once, item 1's entry and item 2's pop in flight
       const int s0 = resolve(__builtin_amdgcn_readfirstlane(pop()));
       const int e0 = s0 >= 0 ? __builtin_amdgcn_readlane(entry_load(s0), 0) : 0;
-      publish_rec(mbox[0], s0 >= 0, s0 >= 0 ? rec_load(e0) : 0, e0);
+      publish_rec(mbox[0], s0 >= 0, s0 >= 0 ? rec_load(e0) : 0, e0, 0);
+      if (lane == 0) mbox[1][6] = -1;
       if (s0 >= 0) {
         const int s1 = resolve(__builtin_amdgcn_readfirstlane(pop()));
         if (s1 >= 0) {
@@ -500,17 +579,16 @@ void prefill_bf16_kernel(PrefillParams p) {
         }
       }
     }
+    // each wave's Q rows of its next item, when it finished the current one early
+    constexpr int QST = D <= 128 ? NW * (D / 16) * 1024 : 16;
+    __shared__ __attribute__((aligned(16))) char qst[QST];
     __syncthreads();
+    bool q_ready = false;                           // this wave's rows of item r are in qst
     for (int r = 0;; ++r) {
       const int* mb = mbox[r & 1];
       if (!mb[5]) break;
       ItemGeo g;
-      g.seq_q0 = g.seq_k0 = mb[0];
-      g.Lq = g.Lk = mb[1];
-      g.q_lo = mb[2] - mb[0];
-      g.q_hi = mb[3] - mb[0];
-      g.hg = mb[4];
-      g.jagged = 1;
+      read_geo(mb, g);
       int rv = 0, e1 = 0;
       bool ok1 = false;
       if (w0) {
@@ -531,9 +609,21 @@ void prefill_bf16_kernel(PrefillParams p) {
         pv_ok = ev_ok;
       }
       int* mo = mbox[(r + 1) & 1];
-      prefill_item<D, QH, NW>(p, smem, g, [&]() {
-        if (w0) publish_rec(mo, ok1, rv, e1);
-      });
+      bool published = false;
+      prefill_item<D, QH, NW, (D <= 128)>(
+          p, smem, g, q_ready,
+          [&](int i, bool last) {
+            if (w0 && !published && (i >= 1 || last)) {
+              publish_rec(mo, ok1, rv, e1, r + 1);
+              published = true;
+            }
+          },
+          [&](ItemGeo& ng) {
+            if (mo[6] != r + 1 || !mo[5]) return false;
+            read_geo(mo, ng);
+            return true;
+          },
+          qst);
     }
   } else {
     // Dense batch, one query tile per workgroup.  XCD-aware order: workgroups
@@ -568,7 +658,8 @@ void prefill_bf16_kernel(PrefillParams p) {
     g.q_lo = qt * BQ;
     g.q_hi = min(g.q_lo + BQ, g.Lq);
     g.jagged = 0;
-    prefill_item<D, QH, NW>(p, smem, g);
+    bool q_ready = false;
+    prefill_item<D, QH, NW>(p, smem, g, q_ready);
   }
 }
 
