@@ -36,7 +36,10 @@ void lse_merge_kernel(MergeParams p) {
   const size_t row = blockIdx.x;
   const size_t rows = (size_t)p.rows;
 
+  // Both loops unrolled so that the loads of several parts are in flight at
+  // once (each part's values are independent; only the sums are ordered).
   float M = neg_inf();
+#pragma unroll 8
   for (int c = grp; c < p.n_parts; c += G) M = fmaxf(M, p.m_parts[(size_t)c * rows + row]);
   if (t == 0) s_m[grp] = M;
   __syncthreads();
@@ -45,14 +48,39 @@ void lse_merge_kernel(MergeParams p) {
   for (int q = 1; q < G; ++q) M = fmaxf(M, s_m[q]);
   const float Mu = (M == neg_inf()) ? 0.f : M;
 
+  // Parts in batches of U: the batch's loads first (indices clamped to the
+  // last part, so every address is valid), then the in-order sums of the
+  // parts that exist.
+  constexpr int U = 4;
   float l = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  for (int c = grp; c < p.n_parts; c += G) {
-    const size_t idx = (size_t)c * rows + row;
-    const float wgt = fast_exp2((p.m_parts[idx] - Mu) * kLog2e);
-    l += wgt * p.l_parts[idx];
-    const f32x4 x = *reinterpret_cast<const f32x4*>(p.o_parts + idx * D + 4 * t);
-    o += wgt * x;
+  if (p.n_parts <= G) {                    // at most one part per group
+    if (grp < p.n_parts) {
+      const size_t idx = (size_t)grp * rows + row;
+      const float wgt = fast_exp2((p.m_parts[idx] - Mu) * kLog2e);
+      l = wgt * p.l_parts[idx];
+      o = wgt * *reinterpret_cast<const f32x4*>(p.o_parts + idx * D + 4 * t);
+    }
+  } else {
+    for (int c0 = grp; c0 < p.n_parts; c0 += U * G) {
+      float mv[U], lv[U];
+      f32x4 ov[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const size_t idx = (size_t)min(c0 + u * G, p.n_parts - 1) * rows + row;
+        mv[u] = p.m_parts[idx];
+        lv[u] = p.l_parts[idx];
+        ov[u] = *reinterpret_cast<const f32x4*>(p.o_parts + idx * D + 4 * t);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (c0 + u * G < p.n_parts) {
+          const float wgt = fast_exp2((mv[u] - Mu) * kLog2e);
+          l += wgt * lv[u];
+          o += wgt * ov[u];
+        }
+      }
+    }
   }
   s_o[grp][t] = o;
   if (t == 0) s_l[grp] = l;
