@@ -38,6 +38,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -65,9 +66,20 @@ _WORKLOAD_FAMILY = {"gqa_ring": "prefill_bf16", "dense_causal": "prefill_bf16", 
                     "decode": "decode", "decode_merge": "decode"}
 
 
+def _code_text(path: str) -> bytes:
+    """A source file without its comments and with whitespace collapsed: a
+    change to comments or layout alone leaves the hash, and so the counter
+    figures taken on that code, unchanged.  (String literals of these files
+    hold no comment markers.)"""
+    text = open(path, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split()).encode()
+
+
 def csrc_hash(workload: str = None) -> str:
-    """Hash of the kernel sources: all of csrc/ (workload None), or the files
-    the given workload's kernels are built from."""
+    """Hash of the kernel code: all of csrc/ (workload None), or the files the
+    given workload's kernels are built from; comments and layout excluded."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "flash_attention_kv_amd", "csrc")
     if workload is None:
@@ -79,7 +91,7 @@ def csrc_hash(workload: str = None) -> str:
         names = sorted(_SHARED_SOURCES + _FAMILY_SOURCES[fam])
     for f in names:
         h.update(f.encode())
-        h.update(open(os.path.join(d, f), "rb").read())
+        h.update(_code_text(os.path.join(d, f)))
     return h.hexdigest()[:16]
 
 

@@ -1,8 +1,10 @@
 // prefill_bf16_kernel.h -- blockwise causal/non-causal prefill attention on gfx950
 // bf16 MFMA with fp32 accumulation.
 //
-// One workgroup (4 waves; 8 for a jagged batch) owns one query tile of QH
-// query heads that share a KV head (GQA), 32 query rows per wave.  It walks the KV chunks in ring order
+// One workgroup of 4 waves owns one query tile of QH query heads that share a
+// KV head (GQA), 32 query rows per wave; jagged batches run persistent 8-wave
+// workgroups that take such work items one after another (the JAG path of
+// prefill_bf16_kernel).  A work item walks the KV chunks in ring order
 // ("_gqa_prefill_long.py": rank r holds chunk (r + s) mod C at step s) and,
 // inside a chunk, the tiles of BK keys up to the dependent end
 // min(chunk end, query tile end) ("[pallas] Support dependent Tile.end bounds
@@ -70,7 +72,8 @@ struct NoNextItem {
 };
 
 // One work item, start to finish: Q rows into registers, the KV walk, the
-// epilogue.  The workgroup's LDS is free on entry and on exit.
+// epilogue.  The K/V stages in LDS are free on entry and on exit (qstage
+// below carries Q rows from one item to the next).
 // on_step(i, last) runs in every wave during tile i of the walk (last: the
 // item's last tile), before that tile's final barrier; an item without tiles
 // still calls it once, as (0, true).
@@ -99,7 +102,6 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
   constexpr int NI = TILE / 16 / (64 * NW);  // DMA instructions per thread per tensor
   static_assert(TILE == 16384 && NI * 64 * NW * 16 == TILE, "tile geometry");
   static_assert(!EARLY || D <= 128, "early hand-over needs the LDS of d <= 128");
-
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -308,12 +310,10 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
           epilogue();
           epi_done = true;
         }
-        if constexpr (EARLY) {
-          ItemGeo ng;
-          if (!q_ready && sidx >= 2 && next_item(ng)) {
-            stage_q(ng);
-            q_ready = true;
-          }
+        ItemGeo ng;
+        if (!q_ready && sidx >= 2 && next_item(ng)) {
+          stage_q(ng);
+          q_ready = true;
         }
       }
     }

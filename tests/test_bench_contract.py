@@ -49,3 +49,12 @@ def test_counter_hash_follows_only_that_kernels_sources():
     assert all("prefill_f32.hip" not in f for f in bench._FAMILY_SOURCES.values())
     assert bench.csrc_hash("gqa_ring") == bench.csrc_hash("jagged") != bench.csrc_hash("decode")
     assert bench.csrc_hash("ring_tiny") == ""
+
+
+def test_counter_hash_ignores_comments_and_layout(tmp_path):
+    a, b, c = tmp_path / "a.hip", tmp_path / "b.hip", tmp_path / "c.hip"
+    a.write_text("int f(int x) {\n  return x + 1;  // one more\n}\n")
+    b.write_text("/* the successor */\nint f(int x) { return x + 1; }\n")
+    c.write_text("int f(int x) { return x + 2; }\n")
+    assert bench._code_text(str(a)) == bench._code_text(str(b))
+    assert bench._code_text(str(a)) != bench._code_text(str(c))
