@@ -30,7 +30,11 @@
  *   - Ownership: the caller owns every buffer, workspaces included.  The
  *     library never allocates, frees or synchronises on these paths; each call
  *     only enqueues kernels on `stream` (a hipStream_t; NULL = null stream)
- *     of the current HIP device, and returns.
+ *     of the current HIP device, and returns.  A workspace holds a call's
+ *     intermediate state (worklists, queue counters, partial triplets) until
+ *     that call's kernels finish: calls that may run at the same time need
+ *     distinct workspaces, while calls ordered on one stream may share one.
+ *     Its contents on entry do not matter.
  *   - Errors: every argument check runs on the host before anything is
  *     enqueued.  An invalid argument returns FAKV_EINVAL, a valid but
  *     unsupported combination FAKV_EUNSUPPORTED; in both cases nothing is
