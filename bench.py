@@ -58,7 +58,8 @@ METRIC = "useful causal TFLOP/s (prefill) and HBM GB/s (split-KV decode), % of r
 # while these files are unchanged, whatever else changes in csrc/.
 _SHARED_SOURCES = ("fakv_device.h", "fakv_kernels.h", "api.hip")
 _FAMILY_SOURCES = {
-    "prefill_bf16": ("prefill_bf16_kernel.h", "prefill_bf16.hip", "prefill_bf16_d256.hip", "worklist.hip"),
+    "prefill_bf16": ("prefill_bf16_kernel.h", "prefill_bf16.hip", "prefill_bf16_d256.hip", "prefill_bf16_jagged.hip",
+                     "worklist.hip"),
     "decode": ("decode.hip", "merge.hip"),
 }
 _WORKLOAD_FAMILY = {"gqa_ring": "prefill_bf16", "dense_causal": "prefill_bf16", "jagged": "prefill_bf16",
@@ -79,7 +80,8 @@ def _code_text(path: str) -> bytes:
 
 def csrc_hash(workload: str = None) -> str:
     """Hash of the kernel code: all of csrc/ (workload None), or the files the
-    given workload's kernels are built from; comments and layout excluded."""
+    given workload's kernels are built from, comments and layout excluded,
+    plus the build flags."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "flash_attention_kv_amd", "csrc")
     if workload is None:
@@ -92,7 +94,18 @@ def csrc_hash(workload: str = None) -> str:
     for f in names:
         h.update(f.encode())
         h.update(_code_text(os.path.join(d, f)))
+    h.update(_build_flags())
     return h.hexdigest()[:16]
+
+
+def _build_flags() -> bytes:
+    """The compiler flags of the library build (build.py's FLAGS without its
+    include paths, and the per-file FILE_FLAGS): they shape the kernel code
+    as much as the sources do."""
+    text = open(os.path.join(ROOT, "flash_attention_kv_amd", "build.py"), encoding="utf-8").read()
+    parts = [m.group(0) for m in re.finditer(r"^(FLAGS|FILE_FLAGS) = [\[{].*?[\]}]$", text, flags=re.S | re.M)]
+    body = " ".join(" ".join(p.split()) for p in parts)
+    return re.sub(r'"-I", os\.path\.join\([^)]*\)', "", body).encode()
 
 
 def load_counter(workload: str, key: str):

@@ -69,6 +69,9 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, int d, int qh, int grid, 
 // d = 256 instances (their own translation unit, see prefill_bf16_d256.hip)
 hipError_t launch_prefill_bf16_d256(const PrefillParams& p, int qh, int grid, hipStream_t stream);
 int prefill_bf16_resident_d256(int qh);
+// jagged d = 64 and 128 instances (their own translation unit, see prefill_bf16_jagged.hip)
+hipError_t launch_prefill_bf16_jagged(const PrefillParams& p, int d, int qh, int grid, hipStream_t stream);
+int prefill_bf16_resident_jagged(int d, int qh);
 hipError_t launch_prefill_f32(const PrefillParams& p, int d, int grid, hipStream_t stream);
 constexpr int kF32QueryTile = 128;   // query rows per fp32 workgroup
 hipError_t launch_decode_partial(const DecodeParams& p, int d, int g, hipStream_t stream);

@@ -1,8 +1,9 @@
 // prefill_bf16.hip -- launch side of the bf16 prefill kernel (the kernel
 // itself is in prefill_bf16_kernel.h): query tile heights, the persistent
-// grid of jagged batches and the dispatch by head dim.  The d = 256
-// instances live in prefill_bf16_d256.hip, built with another instruction
-// scheduling strategy.
+// grid of jagged batches and the dispatch by head dim.  The jagged d = 64
+// and 128 instances live in prefill_bf16_jagged.hip and the d = 256 ones in
+// prefill_bf16_d256.hip, each built with its own instruction scheduling
+// strategy; this unit holds the dense d = 64 and 128 instances.
 #include <atomic>
 
 #include "prefill_bf16_kernel.h"
@@ -24,7 +25,7 @@ int prefill_bf16_persistent_grid(int d, int qh) {
   if (g > 0) return g;
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  const int per = d == 64 ? resident_qh<64>(qh) : d == 128 ? resident_qh<128>(qh) : prefill_bf16_resident_d256(qh);
+  const int per = d == 256 ? prefill_bf16_resident_d256(qh) : prefill_bf16_resident_jagged(d, qh);
   // a multiple of 8 (one share per XCD queue), at least 8
   g = ((per * cus) / 8) * 8;
   if (g < 8) g = 8;
@@ -35,8 +36,8 @@ int prefill_bf16_persistent_grid(int d, int qh) {
 hipError_t launch_prefill_bf16(const PrefillParams& p, int d, int qh, int grid, hipStream_t stream) {
   const bool jagged = p.sched != nullptr;
   switch (d) {
-    case 64: return jagged ? launch_qh<64, true>(p, qh, grid, stream) : launch_qh<64, false>(p, qh, grid, stream);
-    case 128: return jagged ? launch_qh<128, true>(p, qh, grid, stream) : launch_qh<128, false>(p, qh, grid, stream);
+    case 64: return jagged ? launch_prefill_bf16_jagged(p, 64, qh, grid, stream) : launch_qh<64, false>(p, qh, grid, stream);
+    case 128: return jagged ? launch_prefill_bf16_jagged(p, 128, qh, grid, stream) : launch_qh<128, false>(p, qh, grid, stream);
     case 256: return launch_prefill_bf16_d256(p, qh, grid, stream);
   }
   return hipErrorInvalidValue;

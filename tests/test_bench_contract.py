@@ -58,3 +58,9 @@ def test_counter_hash_ignores_comments_and_layout(tmp_path):
     c.write_text("int f(int x) { return x + 2; }\n")
     assert bench._code_text(str(a)) == bench._code_text(str(b))
     assert bench._code_text(str(a)) != bench._code_text(str(c))
+
+
+def test_counter_hash_covers_build_flags():
+    flags = bench._build_flags().decode()
+    assert "FILE_FLAGS" in flags and "prefill_bf16_jagged.hip" in flags and "sched-strategy" in flags
+    assert "/root" not in flags and "os.path" not in flags     # no machine-specific paths
