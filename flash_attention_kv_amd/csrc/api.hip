@@ -44,11 +44,12 @@ int heads_per_wg(int h_q, int h_kv) {
   return (g % 4 == 0) ? 4 : (g % 2 == 0) ? 2 : 1;
 }
 
-// Query rows per workgroup tile; bf16 jagged batches use taller tiles than
-// dense ones (more waves share each K/V tile in LDS).
-int query_tile(int h_q, int h_kv, int d, int dtype, bool jagged) {
+// Query rows per workgroup tile; bf16 jagged batches, and dense d = 128 ones
+// without a sliding window, use taller tiles (more waves share each K/V tile
+// in LDS).
+int query_tile(int h_q, int h_kv, int d, int dtype, bool jagged, bool window = false) {
   if (dtype == FAKV_F32) return fakv::kF32QueryTile;
-  return fakv::prefill_bf16_query_rows(d, heads_per_wg(h_q, h_kv), jagged);
+  return fakv::prefill_bf16_query_rows(d, heads_per_wg(h_q, h_kv), jagged, window);
 }
 
 bool env_no_prune() {
@@ -184,7 +185,7 @@ static fakv_status ring_attn_impl(const void* q, const void* k, const void* v, v
   if (n_seqs < 0 || (seq_offsets == nullptr && n_seqs < 1))
     return fail(FAKV_EINVAL, "n_seqs must be >= 1 for a dense batch (got %d)", n_seqs);
   const bool jagged = seq_offsets != nullptr;
-  const int BQ = query_tile(h_q, h_kv, d, dtype, jagged);
+  const int BQ = query_tile(h_q, h_kv, d, dtype, jagged, causal && window > 0);
   const int qh = dtype == FAKV_BF16 ? heads_per_wg(h_q, h_kv) : 1;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (!jagged) {

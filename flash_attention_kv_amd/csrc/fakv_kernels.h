@@ -63,8 +63,8 @@ struct MergeParams {
 hipError_t ensure_lds_limit(const void* fn, int bytes, std::atomic<unsigned>& done_mask);
 
 // Query rows of one bf16 workgroup tile for head dim d and qh query heads
-// per workgroup, for a dense or a jagged batch.
-int prefill_bf16_query_rows(int d, int qh, bool jagged);
+// per workgroup, for a dense or a jagged batch, with or without a window.
+int prefill_bf16_query_rows(int d, int qh, bool jagged, bool window);
 hipError_t launch_prefill_bf16(const PrefillParams& p, int d, int qh, int grid, hipStream_t stream);
 // d = 256 instances (their own translation unit, see prefill_bf16_d256.hip)
 hipError_t launch_prefill_bf16_d256(const PrefillParams& p, int qh, int grid, hipStream_t stream);

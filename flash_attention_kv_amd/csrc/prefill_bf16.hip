@@ -10,9 +10,8 @@
 
 namespace fakv {
 
-int prefill_bf16_query_rows(int d, int qh, bool jagged) {
-  (void)d;
-  return 32 * ((jagged ? kWavesJagged : kWavesDense) / qh);
+int prefill_bf16_query_rows(int d, int qh, bool jagged, bool window) {
+  return 32 * ((jagged ? kWavesJagged : dense_waves(d, window)) / qh);
 }
 
 // Workgroups of the persistent (jagged) launch: all that fit at once.

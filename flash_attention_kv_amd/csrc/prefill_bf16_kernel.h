@@ -45,8 +45,12 @@ namespace fakv {
 // it by more than this many powers of two.
 constexpr float kLazyShift = 8.f;
 
-// Keys per tile by head dim: every K or V tile is 1024 16-byte slots (16 KB).
-template <int D> struct TileK { static constexpr int BK = 8192 / D; };
+// Keys per tile: 16 KB per K or V tile (8192 / d keys), except for the dense
+// d = 128 instances of 8 waves, which take 128-key (32 KB) tiles -- half the
+// per-tile barriers, row-max reductions and shift checks per FLOP.
+template <int D, int NW, bool JAG> struct TileK {
+  static constexpr int BK = (!JAG && D == 128 && NW == 8) ? 128 : 8192 / D;
+};
 
 __device__ __forceinline__ void wait_dma_and_sync() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -86,21 +90,21 @@ struct NoNextItem {
 // setting q_ready: the next item then reads them from LDS.  Those waves sit
 // out the item's last diagonal tiles anyway, so the next item waits on fewer
 // loads and the output stores overlap the remaining tiles.
-template <int D, int QH, int NW, bool EARLY = false, class StepHook = NoStepHook, class NextItem = NoNextItem>
+template <int D, int QH, int NW, int BK, bool EARLY = false, class StepHook = NoStepHook,
+          class NextItem = NoNextItem>
 __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem, const ItemGeo& g, bool& q_ready,
                                              StepHook on_step = StepHook{}, NextItem next_item = NextItem{},
                                              char* qstage = nullptr) {
-  constexpr int BK = TileK<D>::BK;
   constexpr int WPH = NW / QH;         // waves per query head
   constexpr int BQ = 32 * WPH;         // query rows per tile
   constexpr int KB = BK / 32;          // 32-key MFMA blocks per tile
   constexpr int DS = D / 16;           // k-steps of S^T = K Q^T
   constexpr int DB = D / 32;           // 32-dim blocks of O^T
   constexpr int KS = BK / 16;          // k-steps of O^T += V^T P^T
-  constexpr int TILE = BK * D * 2;     // bytes of one K or V tile (16 KB)
+  constexpr int TILE = BK * D * 2;     // bytes of one K or V tile (16 or 32 KB)
   constexpr int NCH = D / 8;           // 16-byte chunks per key row
   constexpr int NI = TILE / 16 / (64 * NW);  // DMA instructions per thread per tensor
-  static_assert(TILE == 16384 && NI * 64 * NW * 16 == TILE, "tile geometry");
+  static_assert((TILE == 16384 || TILE == 32768) && NI * 64 * NW * 16 == TILE, "tile geometry");
   static_assert(!EARLY || D <= 128, "early hand-over needs the LDS of d <= 128");
 
   const int tid = threadIdx.x;
@@ -325,9 +329,12 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
       // compiler would otherwise wait for the next tile's HBM -> LDS loads
       // (vmcnt(0)) before the first read of this tile, serialising prefetch
       // and compute.
-      constexpr int KOFF = BUF * 2 * TILE;
+      // ds_read offsets are 16-bit immediates: with 32 KB tiles buffer 1
+      // starts past them, so its reads take that base from the address register
+      constexpr int BASE = 4 * TILE > 65536 ? BUF * 2 * TILE : 0;
+      constexpr int KOFF = BUF * 2 * TILE - BASE;
       constexpr int VOFF = KOFF + TILE;
-      const lds_char* lb = (const lds_char*)smem;
+      const lds_char* lb = (const lds_char*)smem + BASE;
       lds_wait();                              // drain scalar loads: counts below are exact
       // S^T = K Q^T, K reads one k-step ahead of the MFMAs
       f32x16 sacc[KB];
@@ -468,13 +475,19 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
   if (!epi_done) epilogue();
 }
 
-// Dense batches run 4 waves per workgroup (two workgroups per CU); jagged
-// batches run 8 (one per CU): two query tiles' worth of rows share every K/V
-// tile brought into LDS -- the "grouping 2" of the Helion page's flattened
-// worklists -- which halves the tile loads per FLOP on the many short tiles
-// of a jagged batch (measured +3 % there, -3 % on the dense d = 256 batch).
+// Dense batches run 4 waves per workgroup (two workgroups per CU), except at
+// d = 128 without a sliding window: 8 waves (one per CU) on 128-key tiles,
+// whose two 64 KB K/V stages leave no room for a second workgroup (measured
+// -4 % time on the 8192-token GQA ring shape, but +5 % with a 2048-key window,
+// whose edge tiles the longer tiles mask more of); jagged batches run 8 (one
+// per CU):
+// two query tiles' worth of rows share every K/V tile brought into LDS --
+// the "grouping 2" of the Helion page's flattened worklists -- which halves
+// the tile loads per FLOP on the many short tiles of a jagged batch
+// (measured +3 % there, -3 % on the dense d = 256 batch).
 constexpr int kWavesDense = 4;
 constexpr int kWavesJagged = 8;
+inline int dense_waves(int d, bool window) { return d == 128 && !window ? 8 : kWavesDense; }
 
 // JAG instances run jagged batches only (persistent, p.sched set), the others
 // dense batches only; each instance holds just its own path, which keeps the
@@ -483,7 +496,8 @@ template <int D, int QH, int NW, bool JAG>
 __global__ __launch_bounds__(64 * NW, 8 / NW)
 void prefill_bf16_kernel(PrefillParams p) {
   constexpr int BQ = 32 * (NW / QH);
-  __shared__ __attribute__((aligned(16))) char smem[4 * 16384];  // K0 V0 K1 V1
+  constexpr int BK = TileK<D, NW, JAG>::BK;
+  __shared__ __attribute__((aligned(16))) char smem[4 * BK * D * 2];  // K0 V0 K1 V1
 
   if constexpr (JAG) {
     // Jagged batch, persistent, drained dynamically.  Queue x holds the
@@ -610,7 +624,7 @@ void prefill_bf16_kernel(PrefillParams p) {
       }
       int* mo = mbox[(r + 1) & 1];
       bool published = false;
-      prefill_item<D, QH, NW, (D <= 128)>(
+      prefill_item<D, QH, NW, BK, (D <= 128)>(
           p, smem, g, q_ready,
           [&](int i, bool last) {
             if (w0 && !published && (i >= 1 || last)) {
@@ -659,24 +673,32 @@ void prefill_bf16_kernel(PrefillParams p) {
     g.q_hi = min(g.q_lo + BQ, g.Lq);
     g.jagged = 0;
     bool q_ready = false;
-    prefill_item<D, QH, NW>(p, smem, g, q_ready);
+    prefill_item<D, QH, NW, BK>(p, smem, g, q_ready);
   }
 }
 
-template <int D, int QH, bool JAG>
+template <int D, int QH, int NW, bool JAG>
 inline hipError_t launch_one(const PrefillParams& p, int grid, hipStream_t stream) {
-  constexpr int NW = JAG ? kWavesJagged : kWavesDense;
   hipLaunchKernelGGL((prefill_bf16_kernel<D, QH, NW, JAG>), dim3(grid), dim3(64 * NW), 0, stream, p);
   return hipGetLastError();
+}
+
+template <int D, int QH, bool JAG>
+inline hipError_t launch_nw(const PrefillParams& p, int grid, hipStream_t stream) {
+  if constexpr (JAG) return launch_one<D, QH, kWavesJagged, true>(p, grid, stream);
+  else if constexpr (D == 128)
+    return dense_waves(D, p.causal && p.window > 0) == 4 ? launch_one<D, QH, 4, false>(p, grid, stream)
+                                                          : launch_one<D, QH, 8, false>(p, grid, stream);
+  else return launch_one<D, QH, kWavesDense, false>(p, grid, stream);
 }
 
 // JAG: the persistent instances of jagged batches (p.sched set), else the dense ones
 template <int D, bool JAG>
 inline hipError_t launch_qh(const PrefillParams& p, int qh, int grid, hipStream_t stream) {
   switch (qh) {
-    case 1: return launch_one<D, 1, JAG>(p, grid, stream);
-    case 2: return launch_one<D, 2, JAG>(p, grid, stream);
-    case 4: return launch_one<D, 4, JAG>(p, grid, stream);
+    case 1: return launch_nw<D, 1, JAG>(p, grid, stream);
+    case 2: return launch_nw<D, 2, JAG>(p, grid, stream);
+    case 4: return launch_nw<D, 4, JAG>(p, grid, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -5,9 +5,12 @@ so two query tiles share each K/V tile brought into LDS ("[pallas] Support
 dependent Tile.end bounds in Pallas", "Flattened worklists": the grouping-2
 work bodies that share a resident cache).  Each wave still owns its 32 query
 rows and visits exactly the tiles those rows admit, in the same ring order,
-so a jagged batch of equal-length sequences must reproduce the dense batch of
-the same sequences bit for bit (chunk width a multiple of both tile heights),
-and both must match the oracle."""
+so where both use key tiles of the same width a jagged batch of equal-length
+sequences must reproduce the dense batch of the same sequences bit for bit
+(chunk width a multiple of both tile heights), and both must match the
+oracle.  Dense d = 128 batches without a window walk 128-key tiles (the
+jagged ones 64-key tiles): the online softmax then folds the keys in other
+groups, so there the two are each held to the oracle instead."""
 import pytest
 import torch
 
@@ -28,7 +31,7 @@ DEV = "cuda:0"
     (128, (8, 2), 4, 300),
     (256, (2, 2), 1, 77),
 ])
-def test_jagged_equal_lengths_match_dense_bitwise(d, heads, C, window):
+def test_jagged_equal_lengths_match_dense(d, heads, C, window):
     h_q, h_kv = heads
     n, L = 3, 1024
     q, k, v = randn([(n * L, h_q, d), (n * L, h_kv, d), (n * L, h_kv, d)], 31 + d + C, "bf16")
@@ -38,10 +41,14 @@ def test_jagged_equal_lengths_match_dense_bitwise(d, heads, C, window):
     jag = F.ring_attn_fwd(qd, kd, vd, C=C, causal=True, seq_offsets=offs, window=window)
     torch.cuda.synchronize()
     assert F.query_tile_rows(h_q, h_kv, d) > 0
-    assert torch.equal(dense, jag), f"d={d} heads={heads} C={C} W={window}"
+    same_tiles = not (d == 128 and window is None)
+    if same_tiles:
+        assert torch.equal(dense, jag), f"d={d} heads={heads} C={C} W={window}"
     # one sequence against the oracle (the others are the same computation)
     ref = oracle.ring_ref(q[:L], k[:L], v[:L], C, causal=True, window=window)
     check(host(jag[:L]), ref, "bf16", f"grouped jagged d={d} {heads} C={C} W={window}")
+    if not same_tiles:
+        check(host(dense[:L]), ref, "bf16", f"dense d={d} {heads} C={C} W={window}")
 
 
 def test_grouped_tile_straddles_sequence_end():
