@@ -458,7 +458,7 @@ def main():
         return
     head = res["gqa_ring"]
     roof = mfma_roofline(head, "gqa_ring")
-    roof["kernel"] = "prefill_bf16_kernel<128, 4, 4, false> (d=128, 4 query heads per 4-wave workgroup, 64-key tiles)"
+    roof["kernel"] = "prefill_bf16_kernel<128, 4, 8, false> (d=128, 4 query heads per 8-wave workgroup, 128-key tiles)"
     roof["useful_flops_per_launch"] = head["flops"]
     line = {
         "metric": METRIC, "value": round(head["tflops"], 2), "unit": "TFLOP/s", "n_gpus": 1,
