@@ -252,8 +252,13 @@ static fakv_status ring_attn_impl(const void* q, const void* k, const void* v, v
   char* ws = static_cast<char*>(workspace);
   int32_t* n_items = reinterpret_cast<int32_t*>(ws);
   int32_t* items = reinterpret_cast<int32_t*>(ws + L.items);
-  hipError_t e = fakv::launch_worklist(seq_offsets, n_seqs, T_q, BQ, items, n_items, (int)cap, st);
-  if (e != hipSuccess) return device_fail("worklist launch", e);
+  // bf16 batches whose tables fit build the worklist and the queues in one launch
+  const bool plan = bf16 && fakv::plan_fits(n_seqs, cap);
+  hipError_t e = hipSuccess;
+  if (!plan) {
+    e = fakv::launch_worklist(seq_offsets, n_seqs, T_q, BQ, items, n_items, (int)cap, st);
+    if (e != hipSuccess) return device_fail("worklist launch", e);
+  }
   fakv::PrefillParams p = base_params(q, k, v, h_q, h_kv, d);
   p.o = static_cast<uint16_t*>(o);
   p.mode = 0;
@@ -270,8 +275,13 @@ static fakv_status ring_attn_impl(const void* q, const void* k, const void* v, v
   sb.seq_of_rank = reinterpret_cast<int32_t*>(ws + L.seq_of_rank);
   sb.sched = reinterpret_cast<int32_t*>(ws + L.sched);
   sb.stride = (int)L.stride;
-  e = fakv::launch_schedule(seq_offsets, n_seqs, BQ, items, n_items, n_hg, sb, st);
-  if (e != hipSuccess) return device_fail("schedule launch", e);
+  if (plan) {
+    e = fakv::launch_plan(seq_offsets, n_seqs, T_q, BQ, items, n_items, (int)cap, n_hg, sb, st);
+    if (e != hipSuccess) return device_fail("plan launch", e);
+  } else {
+    e = fakv::launch_schedule(seq_offsets, n_seqs, BQ, items, n_items, n_hg, sb, st);
+    if (e != hipSuccess) return device_fail("schedule launch", e);
+  }
   p.sched = sb.sched;
   p.sched_stride = sb.stride;
   p.qinfo = sb.qinfo;

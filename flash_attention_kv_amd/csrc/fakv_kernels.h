@@ -90,6 +90,12 @@ struct SchedBufs {
 };
 hipError_t launch_schedule(const int32_t* seq_offsets, int n_seqs, int BQ, const int32_t* items,
                            const int32_t* n_items, int n_hg, const SchedBufs& sb, hipStream_t stream);
+// launch_worklist and launch_schedule in one launch (the same records and
+// queues), for batches of at most 2048 sequences and 12288 worklist slots:
+// plan_fits() says whether a batch qualifies.
+bool plan_fits(int n_seqs, size_t capacity);
+hipError_t launch_plan(const int32_t* seq_offsets, int n_seqs, int total, int BQ, int32_t* items,
+                       int32_t* n_items, int capacity, int n_hg, const SchedBufs& sb, hipStream_t stream);
 // Resident workgroups of the bf16 prefill kernel on the current device (for persistent grids).
 int prefill_bf16_persistent_grid(int d, int qh);
 

@@ -267,6 +267,177 @@ void schedule_kernel(const int32_t* __restrict__ off, int n_seqs, int BQ, const 
   if (tid < 8) sb.qinfo[16 + 4 * tid] = 0;          // the queues' pop counters
 }
 
+// ---------------------------------------------------------------------------
+// worklist_kernel and schedule_kernel fused into one launch, for batches whose
+// per-sequence tables fit in LDS (kPlanSeqs sequences, kPlanItems worklist
+// slots): the same records in the same order, and queues dealt by the same
+// rule.  The sequence starts, tile counts, tile prefix sums, the ranking by
+// tile count and the (sequence, tile) -> record map stay in LDS, so no pass
+// waits on a global load, and each ranking pass takes one barrier (two
+// alternating copies of the per-wave counts).
+constexpr int kPlanSeqs = 2048;
+constexpr int kPlanItems = 12288;
+
+__global__ __launch_bounds__(1024)
+void plan_kernel(const int32_t* __restrict__ off, int n_seqs, int total, int BQ, int32_t* __restrict__ items,
+                 int32_t* __restrict__ n_items, int capacity, int n_hg, SchedBufs sb) {
+  __shared__ int s_wave[2][16];
+  __shared__ int s_w8[128];
+  __shared__ int s_carry[8];
+  __shared__ int s_max, s_bad, s_ranked;
+  __shared__ int s_hist[1025];                 // tile counts 1 .. 1024 (larger ones share the last bin)
+  __shared__ int s_start[kPlanSeqs];
+  __shared__ int s_nt[kPlanSeqs];              // tiles per sequence
+  __shared__ int s_pre[kPlanSeqs + 1];         // exclusive prefix sums of s_nt
+  __shared__ int s_rank[kPlanSeqs];            // sequences by tile count, descending
+  __shared__ int s_idx[kPlanItems];            // (sequence, tile) in natural order -> record index
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  auto bin = [&](int v) { return min(v, 1024); };
+
+  // 1. validate the offsets (direct compares, as in worklist_kernel), lengths
+  //    as tile counts, histogram and prefix sums of the counts
+  for (int i = tid; i < 1025; i += 1024) s_hist[i] = 0;
+  if (tid == 0) { s_max = 0; s_bad = (off[0] != 0 || off[n_seqs] != total) ? 1 : 0; }
+  __syncthreads();
+  int local_max = 0, bad = 0;
+  for (int b = tid; b < n_seqs; b += 1024) {
+    const int a0 = off[b], a1 = off[b + 1];
+    if (a1 < a0) bad = 1;
+    const int L = bad ? 0 : a1 - a0;
+    const int nt = L / BQ + (L % BQ != 0);
+    s_start[b] = a0;
+    s_nt[b] = nt;
+    local_max = max(local_max, nt);
+  }
+  if (bad) atomicOr(&s_bad, 1);
+  atomicMax(&s_max, local_max);
+  __syncthreads();
+  if (s_bad) {                                 // rejected offsets: empty list, empty queues
+    if (tid == 0) *n_items = 0;
+    if (tid < 16) sb.qinfo[tid] = 0;
+    if (tid < 8) sb.qinfo[16 + 4 * tid] = 0;
+    return;
+  }
+  {
+    int carry = 0;
+    for (int b0 = 0; b0 < n_seqs; b0 += 1024) {
+      const int b = b0 + tid;
+      const int v = b < n_seqs ? s_nt[b] : 0;
+      int tot;
+      const int ex = block_exclusive_scan(v, s_wave[0], tot);
+      if (b < n_seqs) {
+        s_pre[b] = carry + ex;
+        if (v > 0) atomicAdd(&s_hist[bin(v)], 1);
+      }
+      carry += tot;
+    }
+    if (tid == 0) s_pre[n_seqs] = carry;
+  }
+  __syncthreads();
+
+  // 2. the worklist: tile index t = T-1 .. 0, sequences with more than t
+  //    tiles in ascending order, ranked by wave ballots
+  const int T = s_max;
+  int base = 0, it = 0;
+  for (int t = T - 1; t >= 0; --t) {
+    for (int b0 = 0; b0 < n_seqs; b0 += 1024, ++it) {
+      const int b = b0 + tid;
+      const bool flag = b < n_seqs && s_nt[b] > t;
+      const unsigned long long bal = __ballot(flag);
+      const int below = __popcll(bal & ((1ull << lane) - 1ull));
+      int* sw = s_wave[it & 1];
+      if (lane == 0) sw[wave] = __popcll(bal);
+      __syncthreads();
+      int pre = 0, tot = 0;
+      for (int w = 0; w < 16; ++w) {
+        const int cnt = sw[w];
+        pre += (w < wave) ? cnt : 0;
+        tot += cnt;
+      }
+      if (flag) {
+        const int pos = base + pre + below;
+        if (pos < capacity) {
+          const int start = s_start[b];
+          const int L = (b + 1 < n_seqs ? s_start[b + 1] : total) - start;
+          const int ts = start + t * BQ;
+          const int ext = min(BQ, L - t * BQ);
+          int32_t* r = items + 8 * (size_t)pos;
+          r[0] = b; r[1] = t; r[2] = start; r[3] = L;
+          r[4] = ts; r[5] = ext; r[6] = min(start + L, ts + ext); r[7] = 0;
+          if (s_pre[b] + t < kPlanItems) s_idx[s_pre[b] + t] = pos;
+        }
+      }
+      base += tot;
+    }
+  }
+  if (tid == 0) *n_items = min(base, capacity);
+  __syncthreads();                             // the last pass's reads of s_wave are done
+
+  // 3. rank the sequences by tile count, descending (as schedule_kernel)
+  {
+    const int v = s_hist[1024 - tid];          // bins from the top: 1024, 1023, .. 1
+    int tot;
+    const int ex = block_exclusive_scan(v, s_wave[0], tot);
+    s_hist[1024 - tid] = ex;                   // now: first rank of the bin
+    __syncthreads();
+    for (int b = tid; b < n_seqs; b += 1024) {
+      const int nt = s_nt[b];
+      if (nt > 0) s_rank[atomicAdd(&s_hist[bin(nt)], 1)] = b;
+    }
+    if (tid == 0) s_ranked = tot;              // non-empty sequences
+    __syncthreads();
+  }
+  const int n_ranked = s_ranked;
+  if (s_hist[1024] > 0 && tid == 0) {          // counts beyond 1024 tiles: order the top bin exactly
+    int n_big = 0;
+    while (n_big < n_ranked && s_nt[s_rank[n_big]] >= 1024) ++n_big;
+    for (int i = 1; i < n_big; ++i) {
+      const int x = s_rank[i];
+      const int vx = s_nt[x];
+      int j = i - 1;
+      while (j >= 0 && s_nt[s_rank[j]] < vx) { s_rank[j + 1] = s_rank[j]; --j; }
+      s_rank[j + 1] = x;
+    }
+  }
+  if (tid < 8) s_carry[tid] = 0;
+  __syncthreads();
+
+  // 4. deal the units (sequence, head group) round-robin onto the 8 queues
+  const int n_units = n_ranked * n_hg;
+  for (int k0 = 0; k0 < n_units; k0 += 1024) {
+    const int k = k0 + tid;
+    const bool valid = k < n_units;
+    const int r = valid ? k / n_hg : 0;
+    const int hg = valid ? k - r * n_hg : 0;
+    const int b = valid ? s_rank[r] : 0;
+    const int v = valid ? s_nt[b] : 0;
+    const int x = tid & 7;                     // == k mod 8 since k0 is a multiple of 1024
+    int tot;
+    const int ex = block_exclusive_scan8(v, s_w8, tot);
+    if (valid) {
+      int32_t* q = sb.sched + (size_t)x * sb.stride + s_carry[x] + ex;
+      const int* nc = s_idx + s_pre[b];
+      for (int j = 0; j < v; ++j) q[j] = nc[v - 1 - j] * n_hg + hg;
+    }
+    __syncthreads();
+    if (tid < 8) s_carry[tid] += tot;
+    __syncthreads();
+  }
+  if (tid < 8) sb.qinfo[tid] = s_carry[tid];
+  if (tid < 8) sb.qinfo[16 + 4 * tid] = 0;     // the queues' pop counters
+}
+
+bool plan_fits(int n_seqs, size_t capacity) {
+  return n_seqs <= kPlanSeqs && capacity <= (size_t)kPlanItems;
+}
+
+hipError_t launch_plan(const int32_t* seq_offsets, int n_seqs, int total, int BQ, int32_t* items,
+                       int32_t* n_items, int capacity, int n_hg, const SchedBufs& sb, hipStream_t stream) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, seq_offsets, n_seqs, total, BQ, items,
+                     n_items, capacity, n_hg, sb);
+  return hipGetLastError();
+}
+
 hipError_t launch_schedule(const int32_t* seq_offsets, int n_seqs, int BQ, const int32_t* items,
                            const int32_t* n_items, int n_hg, const SchedBufs& sb, hipStream_t stream) {
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, stream, seq_offsets, n_seqs, BQ, items,

@@ -236,7 +236,8 @@ fakv_status fakv_jagged_worklist(const int32_t* seq_offsets, int n_seqs, int tot
                                  void* stream);
 
 /* Query-tile height of the worklist ring_attn_fwd builds for a jagged batch
- * with these arguments (its BQ; bf16 dense batches run tiles half as tall).
+ * with these arguments (its BQ; bf16 dense batches run 4-wave tiles half as
+ * tall, except d = 128 without a sliding window, which runs this height).
  * 0 for arguments ring_attn_fwd rejects (h_q not a multiple of h_kv, d). */
 int fakv_query_tile_rows(int h_q, int h_kv, int d, int dtype);
 
