@@ -64,6 +64,7 @@ _FAMILY_SOURCES = {
 }
 _WORKLOAD_FAMILY = {"gqa_ring": "prefill_bf16", "dense_causal": "prefill_bf16", "jagged": "prefill_bf16",
                     "gqa_swa": "prefill_bf16", "jagged_sched": "prefill_bf16", "jagged_worklist": "prefill_bf16",
+                    "jagged_plan": "prefill_bf16",
                     "decode": "decode", "decode_merge": "decode"}
 
 
