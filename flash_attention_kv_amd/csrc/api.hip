@@ -184,6 +184,11 @@ static fakv_status ring_attn_impl(const void* q, const void* k, const void* v, v
   if (C < 1) return fail(FAKV_EINVAL, "C must be >= 1 (got %d)", C);
   if (n_seqs < 0 || (seq_offsets == nullptr && n_seqs < 1))
     return fail(FAKV_EINVAL, "n_seqs must be >= 1 for a dense batch (got %d)", n_seqs);
+  // A window as long as the longest sequence already admits every causal key;
+  // longer ones are clamped to that, so no window bound on the device (query
+  // position - window - key offset, in 32 bits) can wrap.
+  const int longest = T_q > S_kv ? T_q : S_kv;
+  if (window > longest) window = longest;
   const bool jagged = seq_offsets != nullptr;
   const int BQ = query_tile(h_q, h_kv, d, dtype, jagged, causal && window > 0);
   const int qh = dtype == FAKV_BF16 ? heads_per_wg(h_q, h_kv) : 1;
@@ -362,6 +367,12 @@ fakv_status attn_partial(const void* q, const void* k, const void* v, float* m, 
   if (!aligned16(o_acc) || !aligned16(m) || !aligned16(l))
     return fail(FAKV_EINVAL, "m, l and o_acc must be 16-byte aligned");
   if (T_q < 0 || S_chunk < 0) return fail(FAKV_EINVAL, "T_q and S_chunk must be >= 0");
+  // the kernels compare query and key positions in 32-bit arithmetic
+  // (q_pos0 - k_pos0 plus a row or key index): keep every position within 2^29
+  constexpr long long kPosLimit = 1ll << 29;
+  if (q_pos0 < -kPosLimit || k_pos0 < -kPosLimit || (long long)q_pos0 + T_q > kPosLimit ||
+      (long long)k_pos0 + S_chunk > kPosLimit)
+    return fail(FAKV_EINVAL, "positions must lie within [-2^29, 2^29] (q_pos0 %d, k_pos0 %d)", q_pos0, k_pos0);
   if ((long long)T_q * h_q * d >= (1ll << 40) || (long long)S_chunk * h_kv * d >= (1ll << 40))
     return fail(FAKV_EINVAL, "tensor too large");
   if ((s = check_kv_extent(S_chunk, h_kv, d, dtype)) != FAKV_OK) return s;

@@ -82,7 +82,9 @@ typedef enum { FAKV_F32 = 0, FAKV_BF16 = 1 } fakv_dtype;
  *                    its merge with the chunk's triplet (the prefill page's
  *                    online-softmax step); a row with no admissible key keeps
  *                    its state.
- * Preconditions: T_q >= 0, S_chunk >= 0, h_q % h_kv == 0.  T_q == 0 enqueues
+ * Preconditions: T_q >= 0, S_chunk >= 0, h_q % h_kv == 0, and every position
+ * (q_pos0 .. q_pos0 + T_q, k_pos0 .. k_pos0 + S_chunk) within [-2^29, 2^29]
+ * (else FAKV_EINVAL: the kernels compare positions in 32 bits).  T_q == 0 enqueues
  * nothing (the pointers may then be NULL); S_chunk == 0 writes identities
  * (accumulate == 0) or nothing.
  */
@@ -155,7 +157,8 @@ fakv_status ring_attn_fwd(const void* q, const void* k, const void* v, void* o,
  * support.  The KV walk of a query tile starts at the tile holding
  * max(chunk start, tile start - window + 1), chunks wholly below it are
  * skipped, and only tiles crossing either edge of the band are masked.
- * window >= the sequence length gives plain causal attention.  Same layouts,
+ * window >= the sequence length gives plain causal attention (a window longer
+ * than every sequence is taken as the longest sequence's length).  Same layouts,
  * workspace and errors as ring_attn_fwd; window < 1 is FAKV_EINVAL.
  */
 fakv_status ring_attn_fwd_window(const void* q, const void* k, const void* v, void* o,

@@ -118,6 +118,20 @@ def test_other_entry_points_reject():
     assert b"capacity" in L.fakv_last_error()
 
 
+def test_attn_partial_rejects_positions_beyond_32_bit_range():
+    """Query and key positions are compared in 32-bit arithmetic on the device:
+    positions beyond 2^29 (or a chunk reaching past it) are refused on the
+    host, before any HIP call."""
+    L = F.lib()
+    lim = 1 << 29
+    for qp, kp, T, S in ((lim, 0, 4, 4), (0, lim - 2, 4, 4), (-lim - 1, 0, 4, 4), (0, -lim - 5, 4, 4),
+                         (2**31 - 1, -2**31, 4, 4)):
+        assert L.attn_partial(16, 16, 16, 16, 16, 16, T, S, 2, 1, 64, qp, kp, 1, 0, F.BF16, None) == EINVAL, (qp, kp)
+        assert "positions" in F.lib().fakv_last_error().decode()
+    # the limits themselves are accepted by the checks (the call then needs a GPU, so only
+    # the refusal above is exercised here)
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     import flash_attention_kv_amd._binding as B
     monkeypatch.setattr(B, "_lib", None)

@@ -11,7 +11,7 @@ import torch
 import flash_attention_kv_amd as F
 import oracle
 from tests._gpu import check, host
-from workloads import randn
+from workloads import randn, seq_offsets_from_lengths
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -96,3 +96,26 @@ def test_window_pruning_equals_masking_bitwise(d, heads, C, W, monkeypatch):
     monkeypatch.delenv("FAKV_NO_PRUNE")
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("jagged", [False, True])
+def test_window_beyond_any_sequence_is_causal(jagged):
+    """A window far longer than any sequence (2^31 - 1 keys) admits every
+    causal key: plain causal attention (the window bounds are computed in
+    32 bits on the device, so such a window must not wrap them)."""
+    h_q, h_kv, d = 4, 2, 128
+    if jagged:
+        lens = [300, 1, 0, 129]
+        offs = seq_offsets_from_lengths(lens)
+        N = int(offs[-1])
+        q, k, v = randn([(N, h_q, d), (N, h_kv, d), (N, h_kv, d)], 71, "bf16")
+        o = F.ring_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, window=2**31 - 1,
+                            seq_offsets=torch.from_numpy(offs).to(DEV))
+        ref = oracle.attention_ref(q, k, v, causal=True, seq_offsets=offs)
+    else:
+        T = 300
+        q, k, v = randn([(T, h_q, d), (T, h_kv, d), (T, h_kv, d)], 72, "bf16")
+        o = F.ring_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), C=2, causal=True, window=2**31 - 1)
+        ref = oracle.attention_ref(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    check(host(o), ref, "bf16", f"window 2^31-1 jagged={jagged}")
