@@ -8,6 +8,7 @@ there is no fallback of any kind.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import functools
 import os
@@ -110,6 +111,18 @@ def _ptr(t: Optional[torch.Tensor]):
 _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
+_SAME_DEVICE = contextlib.nullcontext()
+
+
+def _on(dev):
+    """The tensors' device made current for the call (the C ABI enqueues on the
+    current HIP device); no device switch when it already is current."""
+    cur = torch.cuda.current_device()
+    if dev.index is None or dev.index == cur:
+        return _SAME_DEVICE
+    return torch.cuda.device(dev.index)
+
+
 def _stream(dev) -> int:
     if _raw_stream is not None:
         return _raw_stream(dev.index if dev.index is not None else torch.cuda.current_device())
@@ -171,16 +184,18 @@ def ring_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, C: int =
     elif need:
         _dev(q, workspace)
     if window is None:
-        st = lib().ring_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), T_q, S_kv, h_q, h_kv, d, C,
-                                 int(causal), _ptr(seq_offsets), n_seqs, dt,
-                                 _ptr(workspace) if need else None, need, _stream(dev))
+        with _on(dev):
+            st = lib().ring_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), T_q, S_kv, h_q, h_kv, d, C,
+                                     int(causal), _ptr(seq_offsets), n_seqs, dt,
+                                     _ptr(workspace) if need else None, need, _stream(dev))
         _check("ring_attn_fwd", st)
     else:
         if not causal:
             raise ValueError("a sliding window needs causal=True")
-        st = lib().ring_attn_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), T_q, S_kv, h_q, h_kv, d, C,
-                                        int(window), _ptr(seq_offsets), n_seqs, dt,
-                                        _ptr(workspace) if need else None, need, _stream(dev))
+        with _on(dev):
+            st = lib().ring_attn_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), T_q, S_kv, h_q, h_kv, d, C,
+                                            int(window), _ptr(seq_offsets), n_seqs, dt,
+                                            _ptr(workspace) if need else None, need, _stream(dev))
         _check("ring_attn_fwd_window", st)
     return o
 
@@ -213,8 +228,9 @@ def attn_partial(q, k, v, *, q_pos0: int = 0, k_pos0: int = 0, causal: bool = Fa
         if m.shape != (T, h_q) or l.shape != (T, h_q) or o.shape != (T, h_q, d):
             raise ValueError("state shapes must be (T, h_q), (T, h_q), (T, h_q, d)")
         acc = 1
-    st = lib().attn_partial(_ptr(q), _ptr(k), _ptr(v), _ptr(m), _ptr(l), _ptr(o), T, n, h_q, h_kv,
-                            d, q_pos0, k_pos0, int(causal), acc, dt, _stream(dev))
+    with _on(dev):
+        st = lib().attn_partial(_ptr(q), _ptr(k), _ptr(v), _ptr(m), _ptr(l), _ptr(o), T, n, h_q, h_kv,
+                                d, q_pos0, k_pos0, int(causal), acc, dt, _stream(dev))
     _check("attn_partial", st)
     return m, l, o
 
@@ -233,8 +249,9 @@ def lse_merge(m_parts, l_parts, o_parts, *, out_dtype=torch.bfloat16, return_lse
         raise ValueError("m_parts and l_parts must be (n_parts, rows)")
     out = torch.empty((rows, d), dtype=out_dtype, device=dev)
     lse = torch.empty(rows, dtype=torch.float32, device=dev) if return_lse else None
-    st = lib().lse_merge(_ptr(m_parts), _ptr(l_parts), _ptr(o_parts), n, rows, d, _ptr(out),
-                         _ptr(lse), BF16 if out_dtype == torch.bfloat16 else F32, _stream(dev))
+    with _on(dev):
+        st = lib().lse_merge(_ptr(m_parts), _ptr(l_parts), _ptr(o_parts), n, rows, d, _ptr(out),
+                             _ptr(lse), BF16 if out_dtype == torch.bfloat16 else F32, _stream(dev))
     _check("lse_merge", st)
     return (out, lse) if return_lse else out
 
@@ -258,8 +275,9 @@ def splitkv_decode(q, k, v, *, n_chunks: int, workspace: Optional[torch.Tensor] 
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     else:
         _dev(q, workspace)
-    st = lib().splitkv_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, h_q, h_kv, d, S, n_chunks, dt,
-                              _ptr(workspace), need, _stream(dev))
+    with _on(dev):
+        st = lib().splitkv_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, h_q, h_kv, d, S, n_chunks, dt,
+                                  _ptr(workspace), need, _stream(dev))
     _check("splitkv_decode", st)
     return o
 
@@ -284,8 +302,9 @@ def splitkv_decode_noalloc(q, k, v, *, n_chunks: int, out: torch.Tensor):
     if Bk != B or dk != d or v.shape != k.shape:
         raise ValueError("shape mismatch between q, k and v")
     o = _out_like(out, q)
-    st = lib().splitkv_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, h_q, h_kv, d, S, n_chunks, dt,
-                                      _stream(dev))
+    with _on(dev):
+        st = lib().splitkv_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, h_q, h_kv, d, S, n_chunks, dt,
+                                          _stream(dev))
     _check("splitkv_decode_noalloc", st)
     return o
 
@@ -297,7 +316,8 @@ def jagged_worklist(seq_offsets: torch.Tensor, total_tokens: int, BQ: int):
     cap = total_tokens // BQ + n_seqs
     items = torch.zeros((max(cap, 1), 8), dtype=torch.int32, device=dev)
     n_items = torch.zeros(1, dtype=torch.int32, device=dev)
-    st = lib().fakv_jagged_worklist(_ptr(seq_offsets), n_seqs, total_tokens, BQ, _ptr(items),
-                                    _ptr(n_items), cap, _stream(dev))
+    with _on(dev):
+        st = lib().fakv_jagged_worklist(_ptr(seq_offsets), n_seqs, total_tokens, BQ, _ptr(items),
+                                        _ptr(n_items), cap, _stream(dev))
     _check("fakv_jagged_worklist", st)
     return items, n_items
