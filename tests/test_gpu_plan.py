@@ -102,3 +102,41 @@ def test_prepass_beyond_item_limit_matches_worklist():
     torch.cuda.synchronize()
     assert n_items == int(ref_n.item())
     assert np.array_equal(w[64:64 + 8 * n_items].reshape(n_items, 8), ref_items[:n_items].cpu().numpy())
+
+
+@pytest.mark.parametrize("n_short", [3, 2100])
+def test_prepass_sequence_beyond_1024_tiles(n_short):
+    """One sequence of more than 1024 query tiles: the ranking by tile count
+    puts it in the histogram's top bin, which both pre-pass paths order by an
+    exact second pass.  With 3 short sequences the fused kernel runs, with 2100
+    the two-kernel path; either way the records equal fakv_jagged_worklist's and
+    every (record, head group) entry is queued once."""
+    h_q = h_kv = 1
+    d = 64
+    BQ = F.query_tile_rows(h_q, h_kv, d)
+    long_len = 1030 * BQ + 17                  # 1031 tiles
+    lens = np.array([5] * (n_short // 2) + [long_len, 2 * BQ + 1] + [1] * (n_short - n_short // 2), dtype=np.int64)
+    offs = seq_offsets_from_lengths(lens)
+    N, n = int(offs[-1]), len(lens)
+    q, k, v = (torch.zeros((N, h, d), dtype=torch.bfloat16, device=DEV) for h in (h_q, h_kv, h_kv))
+    offs_d = torch.from_numpy(offs).to(DEV)
+    need = F.ring_attn_workspace_bytes(N, N, h_q, h_kv, d, 1, True, n, True, F.BF16)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    F.ring_attn_fwd(q, k, v, causal=True, seq_offsets=offs_d, workspace=ws)
+    torch.cuda.synchronize()
+    w = ws.cpu().numpy().view(np.int32)
+    n_items = int(w[0])
+    ref_items, ref_n = F.jagged_worklist(offs_d, N, BQ)
+    torch.cuda.synchronize()
+    assert n_items == int(ref_n.item()) == int(sum((L + BQ - 1) // BQ for L in lens))
+    assert np.array_equal(w[64:64 + 8 * n_items].reshape(n_items, 8), ref_items[:n_items].cpu().numpy())
+    cap = N // BQ + n
+    n_hg = h_q // (256 // BQ)
+    o_sched = (256 + _a256(cap * 32) + _a256(cap * 4) + _a256((n + 1) * 4) + _a256(n * 4)) // 4
+    stride = cap * n_hg
+    qlen = w[16:24]
+    entries = np.concatenate([w[o_sched + x * stride:o_sched + x * stride + int(qlen[x])] for x in range(8)])
+    assert np.array_equal(np.sort(entries), np.arange(n_items * n_hg))
+    # the long sequence is ranked first: its unit heads queue 0, longest query tile first
+    first = w[o_sched] // n_hg
+    assert w[64 + 8 * first] == n_short // 2 and w[64 + 8 * first + 1] == 1030
