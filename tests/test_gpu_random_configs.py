@@ -7,6 +7,8 @@ jagged batch, ring chunk count, causal or not, sliding window, lengths that
 are not tile multiples, empty sequences -- so that combinations nobody wrote
 down still meet the oracle (the plain definition of softmax attention,
 computed in fp64).  Each draw is reproducible from its seed alone."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -18,7 +20,9 @@ from workloads import randn, seq_offsets_from_lengths
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-SEEDS = list(range(1000, 1032))
+# FAKV_EXTRA_SEEDS=N adds N more seeds (2000, 2001, ...) for a wider sweep
+SEEDS = list(range(1000, 1032)) + list(range(2000, 2000 + int(os.environ.get("FAKV_EXTRA_SEEDS", "0"))))
+DECODE_DRAWS = 16 + int(os.environ.get("FAKV_EXTRA_SEEDS", "0")) // 2
 
 
 def _divisors(n, cap=8):
@@ -70,6 +74,28 @@ def test_random_prefill_config(seed):
         ref = oracle.attention_ref(q, k, v, causal=c["causal"], n_seqs=n, window=c["window"])
     torch.cuda.synchronize()
     check(host(o), ref, c["dtype"], tag)
+
+
+def draw_decode(i):
+    """One split-KV decode configuration: batch, GQA group (not only powers of
+    two), head dim, cache length and chunk count (1 <= n_chunks <= S_kv;
+    chunks of ceil(S / n) keys, so the last ones may be short or empty)."""
+    r = np.random.RandomState(7000 + i)
+    h_kv = int(r.choice([1, 2, 4, 8]))
+    g = int(r.choice([1, 2, 3, 4, 8]))
+    S = int(r.randint(1, 3000))
+    return dict(B=int(r.randint(1, 5)), h_q=g * h_kv, h_kv=h_kv, d=int(r.choice([64, 128, 256])), S=S,
+                n_chunks=int(r.randint(1, min(70, S) + 1)))
+
+
+@pytest.mark.parametrize("i", range(DECODE_DRAWS))
+def test_random_decode_config(i):
+    c = draw_decode(i)
+    q, k, v = randn([(c["B"], c["h_q"], c["d"]), (c["B"], c["S"], c["h_kv"], c["d"]),
+                     (c["B"], c["S"], c["h_kv"], c["d"])], 7000 + i, "bf16")
+    o = F.splitkv_decode(q.to(DEV), k.to(DEV), v.to(DEV), n_chunks=c["n_chunks"])
+    torch.cuda.synchronize()
+    check(host(o), oracle.splitkv_decode_ref(q, k, v, c["n_chunks"]), "bf16", str(c))
 
 
 def test_draws_cover_the_space():
