@@ -111,8 +111,9 @@ JaggedLayout jagged_layout(int T_q, int n_seqs, int BQ, int n_hg, bool sched) {
 // empty: the call has no query rows, so no tensor is read and null pointers
 // are accepted.
 fakv_status check_prefill_common(const void* q, const void* k, const void* v, int h_q, int h_kv,
-                                 int d, int dtype, bool empty = false) {
-  if ((!q || !k || !v) && !empty) return fail(FAKV_EINVAL, "q, k and v must be non-null");
+                                 int d, int dtype, bool empty = false, bool no_keys = false) {
+  if ((!q || !k || !v) && !empty && !(no_keys && q))
+    return fail(FAKV_EINVAL, "q, k and v must be non-null");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v))
     return fail(FAKV_EINVAL, "q, k and v must be 16-byte aligned");
   if (h_q < 1 || h_kv < 1) return fail(FAKV_EINVAL, "h_q and h_kv must be >= 1 (got %d, %d)", h_q, h_kv);
@@ -361,7 +362,8 @@ fakv_status attn_partial(const void* q, const void* k, const void* v, float* m, 
                          float* o_acc, int T_q, int S_chunk, int h_q, int h_kv, int d, int q_pos0,
                          int k_pos0, int causal, int accumulate, int dtype, void* stream) {
   g_err.clear();
-  fakv_status s = check_prefill_common(q, k, v, h_q, h_kv, d, dtype, T_q == 0);
+  // an empty chunk (S_chunk == 0) reads no key: k and v may then be NULL
+  fakv_status s = check_prefill_common(q, k, v, h_q, h_kv, d, dtype, T_q == 0, S_chunk == 0);
   if (s != FAKV_OK) return s;
   if ((!m || !l || !o_acc) && T_q != 0) return fail(FAKV_EINVAL, "m, l and o_acc must be non-null");
   if (!aligned16(o_acc) || !aligned16(m) || !aligned16(l))

@@ -86,7 +86,7 @@ typedef enum { FAKV_F32 = 0, FAKV_BF16 = 1 } fakv_dtype;
  * (q_pos0 .. q_pos0 + T_q, k_pos0 .. k_pos0 + S_chunk) within [-2^29, 2^29]
  * (else FAKV_EINVAL: the kernels compare positions in 32 bits).  T_q == 0 enqueues
  * nothing (the pointers may then be NULL); S_chunk == 0 writes identities
- * (accumulate == 0) or nothing.
+ * (accumulate == 0) or nothing, and k, v may then be NULL.
  */
 fakv_status attn_partial(const void* q, const void* k, const void* v,
                          float* m, float* l, float* o_acc,

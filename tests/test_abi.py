@@ -118,6 +118,16 @@ def test_other_entry_points_reject():
     assert b"capacity" in L.fakv_last_error()
 
 
+def test_attn_partial_empty_chunk_accepts_null_kv():
+    """An empty KV chunk reads no key, so k and v may be NULL (torch gives an
+    empty tensor a null data pointer): merging it into a running state is a
+    valid call that enqueues nothing; q must still be given."""
+    L = F.lib()
+    assert L.attn_partial(16, None, None, 16, 16, 16, 4, 0, 2, 1, 64, 0, 0, 1, 1, F.BF16, None) == 0
+    assert L.attn_partial(None, None, None, 16, 16, 16, 4, 0, 2, 1, 64, 0, 0, 1, 1, F.BF16, None) == EINVAL
+    assert L.attn_partial(16, None, 16, 16, 16, 16, 4, 4, 2, 1, 64, 0, 0, 1, 1, F.BF16, None) == EINVAL
+
+
 def test_attn_partial_rejects_positions_beyond_32_bit_range():
     """Query and key positions are compared in 32-bit arithmetic on the device:
     positions beyond 2^29 (or a chunk reaching past it) are refused on the

@@ -180,6 +180,24 @@ def test_attn_partial_empty_chunk_writes_identity():
     assert torch.all(torch.isneginf(m)) and not l.any() and not o.any()
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_attn_partial_empty_chunk_tensors(dtype):
+    """Zero-length K/V tensors (null data pointers): written alone the chunk
+    gives the identity, merged into a running state it leaves the state as it
+    was, bit for bit."""
+    q, k, v = _qkv(40, 24, 4, 2, 128, dtype, 8)
+    qd = q.to(DEV)
+    ke, ve = k[:0].to(DEV), v[:0].to(DEV)
+    m, l, o = F.attn_partial(qd, ke, ve, q_pos0=0, k_pos0=0, causal=False)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isneginf(m)) and not l.any() and not o.any()
+    st = F.attn_partial(qd, k.to(DEV), v.to(DEV), q_pos0=30, k_pos0=0, causal=True)
+    before = [t.clone() for t in st]
+    st = F.attn_partial(qd, ke, ve, q_pos0=30, k_pos0=24, causal=True, state=st)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(before, st))
+
+
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_lse_merge_matches_oracle(out):
     n, rows, d = 9, 50, 128

@@ -98,6 +98,43 @@ def test_random_decode_config(i):
     check(host(o), oracle.splitkv_decode_ref(q, k, v, c["n_chunks"]), "bf16", str(c))
 
 
+PARTIAL_DRAWS = 12 + int(os.environ.get("FAKV_EXTRA_SEEDS", "0")) // 2
+
+
+@pytest.mark.parametrize("i", range(PARTIAL_DRAWS))
+def test_random_partial_chain(i):
+    """A chain of attn_partial calls over KV chunks of random sizes (empty ones
+    included) at random query and key positions, the first written and the
+    rest merged into the running state, against the same chain in the oracle
+    (the prefill page's ring step with explicit positions)."""
+    r = np.random.RandomState(9000 + i)
+    d = int(r.choice([64, 128, 256]))
+    g = int(r.choice([1, 2, 3, 4, 8]))
+    h_kv = int(r.choice([1, 2]))
+    h_q = g * h_kv
+    dtype = "f32" if r.rand() < 0.3 else "bf16"
+    T, q_pos0, causal = int(r.randint(1, 300)), int(r.randint(0, 400)), bool(r.rand() < 0.6)
+    sizes = [int(x) for x in r.randint(0, 250, size=int(r.randint(1, 5)))]
+    k_pos = int(r.randint(0, 300))
+    tag = f"d={d} h={h_q}/{h_kv} {dtype} T={T} q_pos0={q_pos0} causal={causal} chunks={sizes} k_pos0={k_pos}"
+    q, = randn([(T, h_q, d)], 9000 + i, dtype)
+    st, ref = None, None
+    for c, S in enumerate(sizes):
+        k, v = randn([(S, h_kv, d), (S, h_kv, d)], 9500 + 7 * i + c, dtype)
+        st = F.attn_partial(q.to(DEV), k.to(DEV), v.to(DEV), q_pos0=q_pos0, k_pos0=k_pos, causal=causal, state=st)
+        ref = oracle.attn_partial_ref(q, k, v, q_pos0=q_pos0, k_pos0=k_pos, causal=causal, state=ref)
+        k_pos += S
+    torch.cuda.synchronize()
+    m, l, o = (host(x) for x in st)
+    fin = np.isfinite(ref.m)
+    assert np.array_equal(np.isfinite(m), fin), tag
+    assert np.all(l[~fin] == 0) and np.all(o[~fin] == 0), tag
+    if fin.any():
+        np.testing.assert_allclose(m[fin], ref.m[fin], atol=1e-4, rtol=0, err_msg=tag)
+        np.testing.assert_allclose(l[fin], ref.l[fin], rtol=2e-2 if dtype == "bf16" else 1e-5, err_msg=tag)
+        check(o[fin] / l[fin][:, None], ref.O[fin] / ref.l[fin][:, None], dtype, tag, out_bf16=False)
+
+
 def test_draws_cover_the_space():
     """The fixed seeds reach every head dim, both dtypes, both batch kinds,
     windows, ring chunking and non-power-of-two groups."""
