@@ -90,7 +90,9 @@ struct NoNextItem {
 // setting q_ready: the next item then reads them from LDS.  Those waves sit
 // out the item's last diagonal tiles anyway, so the next item waits on fewer
 // loads and the output stores overlap the remaining tiles.
-template <int D, int QH, int NW, int BK, bool EARLY = false, class StepHook = NoStepHook,
+// JAGW: the item runs in a persistent workgroup, whose next item follows at
+// once (no LDS of the K/V stages is free after the walk).
+template <int D, int QH, int NW, int BK, bool EARLY = false, bool JAGW = false, class StepHook = NoStepHook,
           class NextItem = NoNextItem>
 __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem, const ItemGeo& g, bool& q_ready,
                                              StepHook on_step = StepHook{}, NextItem next_item = NextItem{},
@@ -262,8 +264,49 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
   const float scale_log2 = p.scale_log2;
 
   // ---- epilogue: O / l in bf16, or the fp32 triplet ------------------------
+  // Dense workgroups pass their bf16 rows through a wave-private 32 x d slice
+  // of the K/V stages (free once the walk is over), so that each store
+  // instruction writes whole rows -- full 128-byte lines -- instead of 16
+  // bytes of each of 32 rows (measured +1.4 % on the GQA ring shape, +2.5 %
+  // on the dense d = 256 batch).  Persistent jagged workgroups store straight
+  // from registers: the next item's loads reuse the stages at once, and on
+  // their wave-private Q hand-over region the same staging measured -0.8 %.
+  constexpr bool OSTAGE = !JAGW && NW * 32 <= 4 * BK;
+  char* const obuf = smem + wave * (32 * D * 2);
   auto epilogue = [&]() {
     float l_tot = halves_sum(l_run);
+    if constexpr (OSTAGE) {
+      if (p.mode == 0) {
+        const float inv = 1.f / l_tot;           // lanes past the tile: never stored
+        // lane (col, half) holds dims 32 b + 8 g + 4 half .. + 3 of row col;
+        // chunk c (dims 8 c .. 8 c + 7) of row r sits at r * 2d + 16 (c ^ kmask(r)).
+        // The lane index is made opaque so that the lane-dependent addresses
+        // are formed here, not kept in registers across the whole tile loop.
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int ocol = ln & 31;
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            u32x2 x = {pack_bf16x2(oacc[b][4 * g] * inv, oacc[b][4 * g + 1] * inv),
+                       pack_bf16x2(oacc[b][4 * g + 2] * inv, oacc[b][4 * g + 3] * inv)};
+            *reinterpret_cast<u32x2*>(obuf + ocol * (2 * D) + 16 * ((4 * b + g) ^ kmask<D>(ocol)) + 8 * half) = x;
+          }
+        lds_wait();
+        constexpr int RPI = 1024 / (2 * D);      // rows per 1 KB store instruction
+        constexpr int LPR = 64 / RPI;            // lanes per row (its 16-byte chunks)
+        const int nr = min(32, q_hi - qw_lo);
+        uint16_t* orow = p.o + ((size_t)(seq_q0 + qw_lo) * p.h_q + head) * D;
+#pragma unroll
+        for (int i = 0; i < 32 / RPI; ++i) {
+          const int r = RPI * i + ln / LPR, c = ln % LPR;
+          const u32x4 x = *reinterpret_cast<const u32x4*>(obuf + r * (2 * D) + 16 * (c ^ kmask<D>(r)));
+          if (r < nr) *reinterpret_cast<u32x4*>(orow + (size_t)r * p.h_q * D + 8 * c) = x;
+        }
+        return;
+      }
+    }
     if (!qvalid) return;
     if (p.mode == 0) {
       const float inv = 1.f / l_tot;
@@ -624,7 +667,7 @@ void prefill_bf16_kernel(PrefillParams p) {
       }
       int* mo = mbox[(r + 1) & 1];
       bool published = false;
-      prefill_item<D, QH, NW, BK, (D <= 128)>(
+      prefill_item<D, QH, NW, BK, (D <= 128), true>(
           p, smem, g, q_ready,
           [&](int i, bool last) {
             if (w0 && !published && (i >= 1 || last)) {
