@@ -81,7 +81,9 @@ struct NoNextItem {
 // on_step(i, last) runs in every wave during tile i of the walk (last: the
 // item's last tile), before that tile's final barrier; an item without tiles
 // still calls it once, as (0, true).
-// EARLY (persistent jagged workgroups, d <= 128): a wave that no later tile of
+// EARLY (persistent jagged workgroups, d <= 128): every wave brings its Q
+// rows through its own d/16 KB of qstage (whole-row loads, read back into
+// registers before the item's first barrier).  A wave that no later tile of
 // the walk concerns -- one ring chunk, causal, pruned, so key tiles come in
 // increasing order and a tile past the wave's last row ends its share --
 // writes its output at once and, from the third tile on (the next item's
@@ -167,8 +169,12 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
       qreg[s] = __builtin_bit_cast(bf16x8, x);
     }
   };
-  // ... or HBM -> LDS, at this wave's DS KB of qstage (lane l's 16 bytes of
-  // k-step s at 1024 s + 16 l, the register layout); rows past the tile read 0
+  // ... or HBM -> LDS, into this wave's DS KB of qstage by whole-row loads
+  // (lane l of load i brings 16 bytes of row r = RPI i + l / LPR: full
+  // 128-byte lines, not 32 bytes of each of 32 rows), chunk c of row r
+  // landing at r * 2d + 16 (c ^ kmask(r)); rows past the tile read 0.
+  // read_stage() then takes the register layout out of it without bank
+  // conflicts.  Measured +1.6 % on the jagged mix against the register loads.
   auto stage_q = [&](const ItemGeo& gg) {
     const int r0 = gg.q_lo + 32 * qsub;
     const int nr = min(32, gg.q_hi - r0);
@@ -176,17 +182,27 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
     const unsigned ext = nr > 0 ? (unsigned)(nr - 1) * rstride + D * 2 : 0u;
     const __amdgpu_buffer_rsrc_t rs =
         make_rsrc(p.q + ((size_t)(gg.seq_q0 + r0) * p.h_q + gg.hg * QH + hl) * D, ext);
-    const unsigned vo = (unsigned)col * rstride + 16u * half;
+    constexpr int RPI = 1024 / (2 * D);
+    constexpr int LPR = 64 / RPI;
 #pragma unroll
-    for (int s = 0; s < DS; ++s) dma16(rs, vo + 32u * s, qstage + wave * (DS * 1024) + 1024 * s);
+    for (int i = 0; i < DS; ++i) {
+      const int r = RPI * i + lane / LPR, c = (lane % LPR) ^ kmask<D>(r);
+      dma16(rs, (unsigned)r * rstride + 16u * c, qstage + wave * (DS * 1024) + 1024 * i);
+    }
   };
+  auto read_stage = [&]() {
+    const char* src = qstage + wave * (DS * 1024) + col * (2 * D);
+#pragma unroll
+    for (int s = 0; s < DS; ++s)
+      qreg[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + 16 * ((2 * s + half) ^ kmask<D>(col))));
+  };
+  bool q_lds = false;                  // rows of this item still on their way to qstage
   if constexpr (EARLY) {
     if (q_ready) {
-      const char* src = qstage + wave * (DS * 1024) + 16 * lane;
-#pragma unroll
-      for (int s = 0; s < DS; ++s) qreg[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + 1024 * s));
+      read_stage();
     } else {
-      load_q(g);
+      stage_q(g);
+      q_lds = true;
     }
   } else if constexpr (!QSTAGE) {
     load_q(g);
@@ -534,7 +550,15 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, char* smem,
 
   if (walk.valid) issue_tile(walk.kt, 0);
   else on_step(0, true);                     // no tile: the hook still runs once
-  if constexpr (QSTAGE) {
+  if constexpr (EARLY) {
+    // the wave's own staging region: read before the barrier like the dense one
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (q_lds) {
+      read_stage();
+      lds_wait();
+    }
+    __syncthreads();
+  } else if constexpr (QSTAGE) {
     // read before the barrier: past it, other waves load tile 1 into stage 1
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
