@@ -14,10 +14,13 @@ and the 4-chunk fp32 ring latency case.
 Per workload:
   1. settle: the step runs back to back for --settle seconds, which brings the
      GPU from idle to its loaded clock before anything is timed.
-  2. W untimed warm-up steps, then K steps, each bracketed by HIP events
-     recorded on the stream the library launches on (torch's current stream);
-     the timed region is bracketed by device synchronisation.  ms_per_step is
-     the mean of the K event times, median_ms their median.
+  2. W untimed warm-up steps, then K steps back to back between one pair of
+     HIP events recorded on the stream the library launches on (torch's
+     current stream), the timed region bracketed by device synchronisation:
+     ms_per_step is that interval over K.  A second pass of K steps, each
+     between its own pair of events, gives median_ms (the event records
+     between launches add a few microseconds per step, so that pass does not
+     set ms_per_step).
 `roofline.achieved` is the dominant kernel's algorithmic work per launch over
 that mean.  `roofline.traffic` (HBM bytes per launch) and
 `roofline.at_measured_clock` (the peak at the clock the counters measured
@@ -145,20 +148,29 @@ def settle(fn, seconds: float):
 
 
 def time_steps(fn, steps: int, warmup: int, stream):
+    """(mean ms per step of K back-to-back steps, median ms of K steps timed
+    one by one, wall seconds of the back-to-back region)."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mean = start.elapsed_time(end) / steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for a, b in evs:
         a.record(stream)
         fn()
         b.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     per = [a.elapsed_time(b) for a, b in evs]
-    return sum(per) / len(per), statistics.median(per), wall
+    return mean, statistics.median(per), wall
 
 
 def prefill_pairs(w, offs):
